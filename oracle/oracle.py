@@ -1,0 +1,311 @@
+"""Float64 CPU oracle for query-agnostic KV-cache eviction.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow reference that the
+GPU path is checked against.  Only the test suite, the package smoke check and
+the benchmark's CPU-baseline leg may import it; the library and its Python
+binding never do, and it imports nothing from them.
+
+What it computes, step by step, with the passage each step follows:
+
+  partition   KV² summary ("KV²가 전체 문맥 재계산 없이 KV 캐시를 압축한다"),
+              section "어떻게 동작하나": the first few prompt tokens are sinks
+              kept as they are; the rest of the cache is cut into consecutive
+              chunks C_1..C_M of size m (the last one may be shorter).  Each
+              chunk owns its own set of reconstruction queries.
+  attention   same page, section "무엇과 다른가": the reconstruction queries are
+              appended after the prefilled cache and attend the whole cache.
+              The probability a query pays to cache position i is the softmax
+              over all cached positions of q.k_i scaled by 1/sqrt(d) (the
+              usual scaled dot product; the page names no scale).
+  score       same section: a position i in chunk C_r is scored by the largest
+              attention any of C_r's queries pays to it, so one query leaning
+              on a token is enough to keep it.  With grouped-query attention
+              the query heads sharing a KV head are pooled the same way (max).
+  sinks       same section: after all chunks are scored the sink positions get
+              the largest possible score (1.0, the top of a probability).
+  budgets     EpiCache review ("[26'ICML] EpiCache"), section "+α: 레이어별 예산
+              배분": more sensitive layers get a larger share of the cache
+              budget, with sharpness alpha.  Read as k_l proportional to
+              s_l^alpha with the integer total kept exact by largest remainder.
+  select      KV² summary, "무엇과 다른가": the lowest-scoring entries are
+              evicted down to the budget.  Ties go to the lower position, and
+              the kept positions are listed in ascending order.
+  compact     KV² summary, "전제와 한계": serving needs the cache physically
+              compacted per head; the kept rows of K and V are copied out.
+  block loop  EpiCache review, "방법: 3단계" (2) and Fig. 1(b): the history is
+              read block by block and the cache is compressed back to the
+              budget after every block, which bounds peak memory.
+  episodes    EpiCache review, "방법: 3단계" (2) and Fig. 3(b): one compressed
+              cache is built per episode from that episode's prompt queries.
+
+Every pin of these functions lives in tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# partition (KV² summary, "어떻게 동작하나")
+# ---------------------------------------------------------------------------
+
+def chunk_bounds(n_cache: int, n_sinks: int, chunk_size: int) -> List[Tuple[int, int]]:
+    """Half-open position ranges of the chunks that follow the sinks."""
+    if chunk_size < 1:
+        raise ValueError("chunk_size must be positive")
+    bounds = []
+    a = n_sinks
+    while a < n_cache:
+        b = min(a + chunk_size, n_cache)
+        bounds.append((a, b))
+        a = b
+    return bounds
+
+
+def query_rows(r: int, q_per_chunk: int) -> Tuple[int, int]:
+    """Rows of the scoring-query tensor that belong to chunk r."""
+    return r * q_per_chunk, (r + 1) * q_per_chunk
+
+
+# ---------------------------------------------------------------------------
+# attention of the appended queries over the whole cache ("무엇과 다른가")
+# ---------------------------------------------------------------------------
+
+def logits(q_rows: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Scaled dot products q.k / sqrt(d): [n_rows, N]."""
+    d = keys.shape[-1]
+    return (np.asarray(q_rows, np.float64) @ np.asarray(keys, np.float64).T) / math.sqrt(d)
+
+
+def softmax_rows(z: np.ndarray) -> np.ndarray:
+    """Row-wise softmax, max-shifted for range only."""
+    z = np.asarray(z, np.float64)
+    zmax = z.max(axis=1, keepdims=True)
+    e = np.exp(z - zmax)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def attention_probs(q_rows: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Probability each query row pays to every cached key: [n_rows, N]."""
+    return softmax_rows(logits(q_rows, keys))
+
+
+# ---------------------------------------------------------------------------
+# per-position score: chunk-restricted max over queries and grouped heads
+# ---------------------------------------------------------------------------
+
+def chunk_scores(q_group: np.ndarray, keys: np.ndarray, r: int, n_sinks: int,
+                 chunk_size: int, q_per_chunk: int, row_block: int = 64) -> np.ndarray:
+    """Scores of the positions of chunk r for one (layer, KV head).
+
+    q_group: [G, Nq, d] the queries of the G heads that share this KV head.
+    keys:    [N, d].
+    Returns  [|C_r|]: max over heads and over chunk r's queries of the
+    probability paid to each position of C_r (probabilities normalised over
+    the whole cache).
+    """
+    n_cache = keys.shape[0]
+    a, b = chunk_bounds(n_cache, n_sinks, chunk_size)[r]
+    r0, r1 = query_rows(r, q_per_chunk)
+    best = np.zeros(b - a, np.float64)
+    for h in range(q_group.shape[0]):
+        rows = q_group[h, r0:r1]
+        for s0 in range(0, rows.shape[0], row_block):
+            p = attention_probs(rows[s0:s0 + row_block], keys)
+            best = np.maximum(best, p[:, a:b].max(axis=0))
+    return best
+
+
+def unit_scores(q_group: np.ndarray, keys: np.ndarray, n_sinks: int, chunk_size: int,
+                q_per_chunk: int, row_block: int = 64) -> np.ndarray:
+    """Scores of every position of one (layer, KV head): [N], sinks = 1."""
+    n_cache = keys.shape[0]
+    s = np.zeros(n_cache, np.float64)
+    for r, (a, b) in enumerate(chunk_bounds(n_cache, n_sinks, chunk_size)):
+        s[a:b] = chunk_scores(q_group, keys, r, n_sinks, chunk_size, q_per_chunk, row_block)
+    s[:min(n_sinks, n_cache)] = 1.0
+    return s
+
+
+def kv_head_of(h: int, group: int) -> int:
+    """Query head h reads KV head h // G (consecutive grouping)."""
+    return h // group
+
+
+def scores(q: np.ndarray, k: np.ndarray, n_sinks: int, chunk_size: int,
+           q_per_chunk: int, units: Optional[Sequence[Tuple[int, int]]] = None) -> np.ndarray:
+    """Scores [L, Hkv, N] for queries q [L, Hq, Nq, d] over keys k [L, Hkv, N, d].
+
+    ``units`` restricts the work to a list of (layer, kv_head) pairs; the
+    remaining entries are left at NaN.
+    """
+    L, Hq, _, _ = q.shape
+    _, Hkv, N, _ = k.shape
+    if Hq % Hkv:
+        raise ValueError("q_heads must be a multiple of kv_heads")
+    G = Hq // Hkv
+    out = np.full((L, Hkv, N), np.nan)
+    todo = [(l, g) for l in range(L) for g in range(Hkv)] if units is None else units
+    for (l, g) in todo:
+        heads = [h for h in range(Hq) if kv_head_of(h, G) == g]
+        qg = np.asarray(q[l, heads], np.float64)
+        out[l, g] = unit_scores(qg, np.asarray(k[l, g], np.float64), n_sinks,
+                                chunk_size, q_per_chunk)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# per-layer budgets (EpiCache review, "+α: 레이어별 예산 배분")
+# ---------------------------------------------------------------------------
+
+class BudgetError(ValueError):
+    pass
+
+
+def layer_budgets(total: int, n_layers: int, sens: Optional[Sequence[float]] = None,
+                  alpha: float = 0.0, n_cache: Optional[int] = None,
+                  n_sinks: int = 0) -> np.ndarray:
+    """Kept positions per (layer, KV head) for each layer: int64 [L].
+
+    Target shares t_l = T * s_l^alpha / sum_j s_j^alpha (uniform when sens is
+    None).  Each layer gets floor(t_l); the T - sum floor(t) leftover units go
+    one each to the layers with the largest fractional parts, lower layer
+    first on equal parts.  A result outside [n_sinks, n_cache] is an error.
+    """
+    if n_layers < 1:
+        raise BudgetError("need at least one layer")
+    if total < 0:
+        raise BudgetError("negative total budget")
+    if sens is None:
+        w = np.ones(n_layers, np.float64)
+    else:
+        s = np.asarray(sens, np.float64)
+        if s.shape != (n_layers,) or not np.all(np.isfinite(s)) or np.any(s <= 0):
+            raise BudgetError("sensitivities must be finite and positive, one per layer")
+        if not (math.isfinite(alpha) and alpha >= 0):
+            raise BudgetError("alpha must be finite and non-negative")
+        w = np.array([float(x) ** float(alpha) for x in s])
+    share = total * w / w.sum()
+    base = np.floor(share).astype(np.int64)
+    left = int(total - base.sum())
+    frac = share - base
+    order = sorted(range(n_layers), key=lambda l: (-frac[l], l))
+    for l in order[:left]:
+        base[l] += 1
+    if n_cache is not None and (np.any(base < n_sinks) or np.any(base > n_cache)):
+        raise BudgetError("a layer budget falls outside [n_sinks, n_cache]")
+    return base
+
+
+# ---------------------------------------------------------------------------
+# selection (KV² summary, "무엇과 다른가": evict the lowest to the budget)
+# ---------------------------------------------------------------------------
+
+def select_unit(s: np.ndarray, k: int, n_sinks: int) -> np.ndarray:
+    """Ascending kept positions: the sinks plus the k - S best of the rest.
+
+    "Best" orders by score descending, then position ascending.
+    """
+    s = np.asarray(s, np.float64)
+    n = s.shape[0]
+    s0 = min(n_sinks, n)
+    if not (s0 <= k <= n):
+        raise BudgetError("budget must lie in [n_sinks, n_cache]")
+    cand = np.arange(s0, n)
+    order = np.lexsort((cand, -s[s0:]))          # primary: -score, then position
+    chosen = cand[order[: k - s0]]
+    return np.sort(np.concatenate([np.arange(s0), chosen])).astype(np.int64)
+
+
+def select(score: np.ndarray, k_per_layer: Sequence[int], n_sinks: int) -> List[np.ndarray]:
+    """Per layer an int64 array [Hkv, k_l] of kept positions."""
+    L, Hkv, _ = score.shape
+    return [np.stack([select_unit(score[l, g], int(k_per_layer[l]), n_sinks)
+                      for g in range(Hkv)]) for l in range(L)]
+
+
+def pack_kept(kept: List[np.ndarray]) -> np.ndarray:
+    """Layer after layer, head after head: the flat kept-index layout."""
+    return np.concatenate([x.reshape(-1) for x in kept]) if kept else np.zeros(0, np.int64)
+
+
+# ---------------------------------------------------------------------------
+# headwise compaction (KV² summary, "전제와 한계")
+# ---------------------------------------------------------------------------
+
+def compact(k: np.ndarray, v: np.ndarray, kept: List[np.ndarray]):
+    """Per layer (K_out [Hkv, k_l, d], V_out [Hkv, k_l, d]): rows K[l, g, kept]."""
+    outs = []
+    for l, kl in enumerate(kept):
+        ko = np.stack([np.take(k[l, g], kl[g], axis=0) for g in range(kl.shape[0])])
+        vo = np.stack([np.take(v[l, g], kl[g], axis=0) for g in range(kl.shape[0])])
+        outs.append((ko, vo))
+    return outs
+
+
+# ---------------------------------------------------------------------------
+# one compression call and the two drivers
+# ---------------------------------------------------------------------------
+
+def compress(q, k, v, n_sinks: int, chunk_size: int, q_per_chunk: int,
+             k_per_layer: Sequence[int]) -> Dict[str, object]:
+    """Score, select and compact one cache."""
+    sc = scores(q, k, n_sinks, chunk_size, q_per_chunk)
+    kept = select(sc, k_per_layer, n_sinks)
+    return {"scores": sc, "kept": kept, "out": compact(k, v, kept)}
+
+
+def block_loop(k_tokens: np.ndarray, v_tokens: np.ndarray, q_steps: np.ndarray,
+               block_len: int, budget_m: int, n_sinks: int,
+               teacher: Optional[Dict[int, Tuple[np.ndarray, np.ndarray, np.ndarray]]] = None):
+    """EpiCache-style block prefill with compression after every block.
+
+    k_tokens, v_tokens: [L, Hkv, T, d]; q_steps: [n_blocks, L, Hq, nq, d].
+    After appending block b the cache holds n rows; if n exceeds the budget M
+    it is scored with block b's queries (one chunk covering every non-sink
+    position) and compacted back to M rows per (layer, KV head).
+
+    Returns a list with one record per block: the cache it started from,
+    the original token positions of each row, and (for scoring steps) the
+    scores and kept positions.  ``teacher`` maps a block index to a cache
+    (k, v, positions) that replaces the running cache before that block's
+    append, so each step can be checked from a common starting point.
+    """
+    L, Hkv, T, d = k_tokens.shape
+    n_blocks = q_steps.shape[0]
+    ck = np.zeros((L, Hkv, 0, d), k_tokens.dtype)
+    cv = np.zeros((L, Hkv, 0, d), v_tokens.dtype)
+    pos = np.zeros((L, Hkv, 0), np.int64)
+    recs = []
+    for b in range(n_blocks):
+        if teacher is not None and b in teacher:
+            ck, cv, pos = teacher[b]
+        a0, a1 = b * block_len, min((b + 1) * block_len, T)
+        ck = np.concatenate([ck, k_tokens[:, :, a0:a1]], axis=2)
+        cv = np.concatenate([cv, v_tokens[:, :, a0:a1]], axis=2)
+        pos = np.concatenate([pos, np.broadcast_to(np.arange(a0, a1), (L, Hkv, a1 - a0))], axis=2)
+        n = ck.shape[2]
+        rec = {"block": b, "n_cache": n, "k": ck, "v": cv, "pos": pos}
+        if n > budget_m:
+            chunk = max(n - n_sinks, 1)
+            sc = scores(q_steps[b], ck, n_sinks, chunk, q_steps.shape[3])
+            kept = select(sc, [budget_m] * L, n_sinks)
+            kk = np.stack(kept)                         # [L, Hkv, M]
+            ck = np.take_along_axis(ck, kk[..., None], axis=2)
+            cv = np.take_along_axis(cv, kk[..., None], axis=2)
+            pos = np.take_along_axis(pos, kk, axis=2)
+            rec.update(scores=sc, kept=kept)
+        recs.append(rec)
+    return recs
+
+
+def episodic(k, v, q_episodes, sens, alpha: float, total: int, n_sinks: int,
+             chunk_size: int, q_per_chunk: int):
+    """One compressed cache per episode, each with sensitivity-split budgets."""
+    L, _, N, _ = k.shape
+    kl = layer_budgets(total, L, sens, alpha, n_cache=N, n_sinks=n_sinks)
+    return kl, [compress(q_episodes[e], k, v, n_sinks, chunk_size, q_per_chunk, kl)
+                for e in range(q_episodes.shape[0])]
