@@ -1,0 +1,257 @@
+"""Throughput of the eviction hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one batch of synthetic input.  For
+the default workload (EpiCache-style block prefill, Llama-3.2-3B shape: 28
+layers, 24 query / 8 KV heads, d=128, bf16, 8 blocks of 2048 tokens, budget
+4096) a step is the full 8-block loop: 8 block appends and 6 compressions
+(score, select, compact) of a 6144-row cache back to 4096 rows.  Inputs are
+generated directly in HBM before timing starts.
+
+Prints one JSON line: the metric (scored cache tokens per second, i.e.
+layers x KV heads x N summed over the scoring calls, per second), the roofline
+of the dominant kernel from HIP events recorded around every launch inside
+the timed region, the per-kernel averages, and the float64 CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+METRIC = "scored cache tokens/sec (Σ layers×kv_heads×N) + % peak MFMA; compact GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="epicache_block_loop",
+                    choices=["epicache_block_loop", "kv2_32k", "kv2_131k", "episodic", "tiny"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true",
+                    help="time without per-launch events (for profiler runs)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "the eviction path is measured per GPU; see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_compression_kvs_amd as K
+    from kv_cache_compression_kvs_amd import drivers
+    from workloads import FULL, gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if not os.path.exists(K.LIB_PATH):
+        from kv_cache_compression_kvs_amd import build as _b
+        _b.build()
+    dev = torch.device("cuda:0")
+    w = FULL[args.workload]
+    s = w.shape
+    t_gen = time.perf_counter()
+
+    # ---- build the step -------------------------------------------------------
+    if w.kind == "block_loop":
+        x = gen.block_loop_inputs(w, device=dev)
+        loop = drivers.BlockLoop(s.layers, s.q_heads, s.kv_heads, s.head_dim, torch.bfloat16,
+                                 w.block_len, w.budget_m, s.n_sinks, s.q_per_chunk, device=dev)
+        calls = []
+        n = 0
+        for b in range(w.n_blocks):
+            n += w.block_len
+            if n > w.budget_m:
+                calls.append(n)
+                n = w.budget_m
+        n_step = calls[0]
+        keep = w.budget_m
+
+        def step():
+            loop.run(x["k_tokens"], x["v_tokens"], x["q_steps"])
+        kl = [keep] * s.layers
+    else:
+        if w.kind == "episodic":
+            x = gen.episodic_inputs(w, device=dev)
+            qs = x["q_episodes"]
+            kl = list(K.kvs_layer_budgets(s.layers, w.total_budget, x["sens"], w.alpha,
+                                          s.n_cache, s.n_sinks))
+            total, sens, alpha = w.total_budget, x["sens"], w.alpha
+        else:
+            x = gen.single_inputs(w, device=dev)
+            qs = x["q"][None]
+            keep = w.keep_per_layer()
+            kl = [keep] * s.layers
+            total, sens, alpha = keep * s.layers, None, 0.0
+        calls = [s.n_cache] * qs.shape[0]
+        n_step = s.n_cache
+        p = K.make_problem(s.layers, s.q_heads, s.kv_heads, s.head_dim, s.n_cache, s.n_sinks,
+                           s.chunk_size, s.q_per_chunk, x["k"].dtype)
+        rows = s.kv_heads * int(sum(kl))
+        scores = torch.empty(s.layers * s.kv_heads * s.n_cache, device=dev)
+        kept = torch.empty(rows, dtype=torch.int32, device=dev)
+        ko = torch.empty(rows, s.head_dim, dtype=x["k"].dtype, device=dev)
+        vo = torch.empty(rows, s.head_dim, dtype=x["k"].dtype, device=dev)
+        ws = K.workspace(p, dev)
+
+        def step():
+            for e in range(qs.shape[0]):
+                K.kvs_compress_block(p, qs[e], x["k"], x["v"], total, sens, alpha, scores, kept,
+                                     ko, vo, 0, ws=ws)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    # ---- timed region -----------------------------------------------------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K.kvs_trace_summary()  # drop anything recorded so far
+    K.kvs_trace_enable(not args.no_trace)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    K.kvs_trace_enable(False)
+    trace = K.kvs_trace_summary()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # ---- algorithmic counts per step ------------------------------------------
+    L, Hq, Hkv, d = s.layers, s.q_heads, s.kv_heads, s.head_dim
+    eb = s.elem_bytes()
+    tokens = sum(L * Hkv * n for n in calls)
+    shp = [s.__class__(L, Hq, Hkv, d, n, s.n_sinks,
+                       (n - s.n_sinks) if w.kind == "block_loop" else s.chunk_size,
+                       s.q_per_chunk, s.dtype) for n in calls]
+    p1_flops = [2 * d * sh.pass1_pairs() for sh in shp]
+    all_flops = sum(sh.counted_flops() for sh in shp)
+    kept_rows = [Hkv * int(sum(kl))] * len(calls)
+    sel_bytes = sum(4 * L * Hkv * n + 4 * r for n, r in zip(calls, kept_rows))
+    cmp_bytes = sum(r * (2 * d * eb * 2 + 4) for r in kept_rows)
+
+    def avg(name):
+        e = trace.get(name)
+        return e["avg_ms"] if e else None
+
+    def tot(name):
+        e = trace.get(name)
+        return e["total_ms"] / args.steps if e else 0.0
+
+    p1_name = "score_pass1_bf16" if s.dtype == "bf16" else "score_pass1_f32"
+    p2_name = "score_pass2_bf16" if s.dtype == "bf16" else "score_pass2_f32"
+    peak = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_FP32_TFLOPS
+    roofline = None
+    if avg(p1_name):
+        # per launch: the pass-1 flops of one scoring call (all calls share a shape
+        # in the block loop and the single-shot workloads)
+        per_launch = p1_flops[0]
+        achieved = per_launch / (avg(p1_name) * 1e-3) / 1e12
+        roofline = {"kernel": p1_name, "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "traffic": None, "flops_per_launch": per_launch,
+                    "avg_launch_ms": round(avg(p1_name), 5)}
+    score_ms = tot(p1_name) + tot("score_merge_splits") + tot(p2_name)
+    sc_ms = tot("select") + tot("compact")
+    kernels = {k: {"avg_ms": round(v["avg_ms"], 5), "count_per_step": v["count"] / args.steps}
+               for k, v in trace.items()}
+
+    rec = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "n_cache_per_call": n_step, "scoring_calls_per_step": len(calls),
+                   "scored_tokens_per_step": tokens, "keep_per_layer": kl[0] if kl else None,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "score_mfma_frac": round(all_flops / (score_ms * 1e-3) / 1e12 / peak, 4) if score_ms else None,
+        "select_compact_GBps": round((sel_bytes + cmp_bytes) / (sc_ms * 1e-3) / 1e9, 1) if sc_ms else None,
+        "select_compact_hbm_frac": round((sel_bytes + cmp_bytes) / (sc_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
+        if sc_ms else None,
+        "kernels": kernels,
+        "input_generation_s": round(t_gen, 2),
+    }
+
+    # ---- float64 oracle on a bounded sample of the same workload ---------------
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, kl)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, x, budget_s, kl):
+    """The oracle, as it is, on whole (layer, KV head) units of one scoring call,
+    until about budget_s seconds have been spent; reported in the metric's unit."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import oracle as O
+
+    s = w.shape
+    if w.kind == "block_loop":
+        n = w.budget_m + w.block_len             # the first scoring call sees tokens [0, n)
+        k_all = x["k_tokens"][:, :, :n]
+        q_all = x["q_steps"][2]
+        chunk = n - s.n_sinks
+    else:
+        n = s.n_cache
+        k_all = x["k"]
+        q_all = x["q_episodes"][0] if w.kind == "episodic" else x["q"]
+        chunk = s.chunk_size
+    G = s.group
+    done_tokens, spent, units = 0, 0.0, 0
+    for l in range(s.layers):
+        for g in range(s.kv_heads):
+            qg = q_all[l, g * G:(g + 1) * G].float().cpu().numpy().astype(np.float64)
+            kg = k_all[l, g].float().cpu().numpy().astype(np.float64)
+            t = time.perf_counter()
+            sc = O.unit_scores(qg, kg, s.n_sinks, chunk, s.q_per_chunk)
+            O.select_unit(sc, int(kl[l]), s.n_sinks)
+            spent += time.perf_counter() - t
+            done_tokens += n
+            units += 1
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    return {"value": done_tokens / spent, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{units} (layer, KV head) units of one {n}-position scoring call of "
+                      f"{w.name}: float64 scores and selection, {spent:.1f} s",
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+/*
+ * kvs.h: C ABI of libkvs, query-agnostic KV-cache eviction on MI355X (gfx950).
+ *
+ * The method (sources, cited by page title and section):
+ *   - KV² summary, "KV²가 전체 문맥 재계산 없이 KV 캐시를 압축한다":
+ *       "어떻게 동작하나": a few leading sink tokens are kept as they are; the
+ *       rest of the prefilled cache is cut into chunks of size m, and each chunk
+ *       owns a set of reconstruction queries.
+ *       "무엇과 다른가": those queries are appended after the cache and attend
+ *       the whole cache; the score of a position in chunk C_r is the largest
+ *       attention any of C_r's queries pays to it; after every chunk is scored
+ *       the sinks are pinned to the top score and the lowest entries are
+ *       evicted down to the budget.
+ *       "전제와 한계": serving needs the cache compacted per head, which a
+ *       masking backend does not do.
+ *   - EpiCache review, "[26'ICML] EpiCache":
+ *       "방법: 3단계" (2) and Fig. 1(b): the history is read block by block and
+ *       the cache is compressed back to a fixed budget after every block, using
+ *       an episode's prompt as the scoring queries.
+ *       "+α: 레이어별 예산 배분": sensitive layers get a larger share of the
+ *       budget, with sharpness alpha.
+ *
+ * Conventions shared by every entry point:
+ *   - Device tensors are caller-owned, row-major and contiguous unless a stride
+ *     argument says otherwise, and 16-byte aligned.  The library keeps no
+ *     pointer after a call returns and allocates no device memory; scratch
+ *     space comes from a caller workspace sized by kvs_workspace_bytes().
+ *   - Every device call only enqueues work on `stream` (a hipStream_t passed as
+ *     void*; NULL is the default stream).  Outputs are valid once the stream
+ *     has reached that point.  No call synchronises the device.
+ *   - Return value: a kvs_status.  Arguments are validated before anything is
+ *     enqueued; on any error other than KVS_E_HIP the outputs are untouched.
+ *     KVS_E_HIP means a launch failed and the outputs are undefined.
+ *   - Scores are fp32 in [0, 1]; kept positions are int32 and ascending within
+ *     each (layer, KV head).
+ */
+#ifndef KVS_H_
+#define KVS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest layer count the per-layer tables carry in kernel arguments. */
+#define KVS_MAX_LAYERS 256
+
+typedef enum kvs_status {
+  KVS_OK = 0,
+  KVS_E_NULL = 1,      /* a required pointer is NULL */
+  KVS_E_SHAPE = 2,     /* sizes inconsistent or unsupported */
+  KVS_E_DTYPE = 3,     /* element type not supported */
+  KVS_E_BUDGET = 4,    /* a budget outside [n_sinks, n_cache], or bad sensitivities */
+  KVS_E_ALIGN = 5,     /* a device pointer is not 16-byte aligned */
+  KVS_E_WORKSPACE = 6, /* workspace smaller than kvs_workspace_bytes() */
+  KVS_E_HIP = 7        /* a HIP launch or runtime call failed */
+} kvs_status;
+
+typedef enum kvs_dtype {
+  KVS_F32 = 0,  /* float32 queries and keys (scored with fp32 vector arithmetic) */
+  KVS_BF16 = 1  /* bfloat16 queries and keys (scored on bf16 MFMA, fp32 accumulate) */
+} kvs_dtype;
+
+/*
+ * One scoring problem.  L = layers, Hq / Hkv = query / KV heads (Hq a multiple
+ * of Hkv, G = Hq/Hkv; query head h reads KV head h / G), d = head_dim in {64,128},
+ * N = n_cache, S = n_sinks, m = chunk_size >= 1, nq = q_per_chunk >= 1.
+ * Chunk r covers positions [S + r*m, min(S + (r+1)*m, N)) for
+ * r < R = ceil((N - S) / m) (R = 0 when N <= S), and owns query rows
+ * [r*nq, (r+1)*nq); the query tensor therefore has Nq = R*nq rows per head.
+ *
+ * Layouts:
+ *   Q       [L, Hq, Nq, d]  of dtype
+ *   K, V    [L, Hkv, kv_row_stride, d] of dtype; rows [0, N) of every
+ *           (layer, KV head) slab are read.  kv_row_stride = 0 means N.
+ *   scores  [L, Hkv, N] fp32
+ */
+typedef struct kvs_problem {
+  int32_t layers;
+  int32_t q_heads;
+  int32_t kv_heads;
+  int32_t head_dim;
+  int64_t n_cache;
+  int64_t n_sinks;
+  int64_t chunk_size;
+  int64_t q_per_chunk;
+  int64_t kv_row_stride;
+  int32_t dtype;   /* kvs_dtype */
+  int32_t flags;   /* reserved, must be 0 */
+} kvs_problem;
+
+/* Text for a status code (static storage; never NULL). */
+const char* kvs_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int kvs_version(void);
+
+/* Pure host check of a problem description; touches no device. */
+int kvs_check_problem(const kvs_problem* p);
+
+/* Number of chunks R and scoring queries per head Nq = R * nq (host only). */
+int64_t kvs_num_chunks(const kvs_problem* p);
+int64_t kvs_num_queries(const kvs_problem* p);
+
+/* Bytes of device workspace kvs_score, kvs_select and kvs_compress_block need
+ * for this problem (0 if the problem is invalid).  Host only. */
+size_t kvs_workspace_bytes(const kvs_problem* p);
+
+/*
+ * Per-layer budgets (EpiCache review, "+α: 레이어별 예산 배분"), host only.
+ * Writes k_out[l], the kept positions per KV head of layer l, sinks included.
+ * With sens == NULL the split is uniform; otherwise layer l's share is
+ * T * sens[l]^alpha / sum_j sens[j]^alpha.  Each layer gets the floor of its
+ * share and the leftover units go one each to the largest fractional parts,
+ * lower layer first on ties, so sum(k_out) == total exactly.
+ * Errors: KVS_E_NULL (k_out), KVS_E_SHAPE (layers outside [1, KVS_MAX_LAYERS]),
+ * KVS_E_BUDGET (total < 0, a sensitivity not finite and > 0, alpha not finite
+ * and >= 0, or any k_out[l] outside [n_sinks, n_cache]).  k_out is written
+ * only on success.
+ */
+int kvs_layer_budgets(int32_t layers, int64_t total, const double* sens, double alpha,
+                      int64_t n_cache, int64_t n_sinks, int64_t* k_out);
+
+/*
+ * Scores (KV² summary, "무엇과 다른가"): for every (layer l, KV head g) and
+ * position i of chunk r,
+ *     scores[l,g,i] = max over heads h of group g and rows j of chunk r of
+ *                     softmax_i'( q[l,h,j] . k[l,g,i'] / sqrt(d) )[i]
+ * with the softmax over all N positions; sink positions i < S get 1.0.
+ * q, k: device, per the layouts above.  scores: device [L, Hkv, N] fp32, fully
+ * written.  ws: device workspace of at least kvs_workspace_bytes(p) bytes.
+ */
+int kvs_score(const kvs_problem* p, const void* q, const void* k, float* scores,
+              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Selection (KV² summary, "무엇과 다른가": evict the lowest to the budget).
+ * For each (l, g) keeps [0, S) plus the k_l - S positions of [S, N) that come
+ * first in the order (score descending, position ascending), and writes them
+ * ascending.  k_per_layer: HOST array [L] with S <= k_l <= N.
+ * kept: device int32, packed layer after layer and head after head: the list
+ * of (l, g) starts at Hkv * sum_{l'<l} k_l' + g * k_l and has k_l entries.
+ * Scores compare as floats (-0 equals +0); NaN orders above +inf.
+ */
+int kvs_select(const kvs_problem* p, const float* scores, const int64_t* k_per_layer,
+               int32_t* kept, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Headwise compaction (KV² summary, "전제와 한계"): copies row kept[.., t] of
+ * each (l, g) slab of K and V to output row t of that slab, bit for bit.
+ * kept: device int32 in kvs_select's packed layout.  An entry outside [0, N) is
+ * skipped: its output row is left as it was.
+ * k_per_layer: HOST [L].
+ * k_out, v_out: device.  out_row_stride == 0: packed like kept (row
+ * Hkv * sum_{l'<l} k_l' + g * k_l + t).  out_row_stride > 0: slab (l, g)
+ * starts at row (l * Hkv + g) * out_row_stride (needs k_l <= out_row_stride).
+ * The outputs must not overlap K or V.
+ */
+int kvs_compact(const kvs_problem* p, const void* k, const void* v, const int32_t* kept,
+                const int64_t* k_per_layer, void* k_out, void* v_out,
+                int64_t out_row_stride, void* stream);
+
+/*
+ * One full compression of a prefilled cache: kvs_layer_budgets, kvs_score,
+ * kvs_select and kvs_compact in sequence.  total_budget, sens and alpha are
+ * as in kvs_layer_budgets (with n_cache = N); the chosen budgets are written
+ * to the HOST array k_per_layer_out [L] when it is not NULL.  If
+ * total_budget >= L * N every position is kept (the cache is copied through
+ * and scores are still written).  scores, kept, k_out, v_out, out_row_stride
+ * and ws are as in the calls above; kept needs Hkv * sum_l k_l entries.
+ */
+int kvs_compress_block(const kvs_problem* p, const void* q, const void* k, const void* v,
+                       int64_t total_budget, const double* sens, double alpha,
+                       float* scores, int32_t* kept, void* k_out, void* v_out,
+                       int64_t out_row_stride, int64_t* k_per_layer_out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Block append for the block-prefill loop (EpiCache review, "방법: 3단계" (2),
+ * Fig. 1(b)): for each of `slabs` (layer, KV head) slabs copies rows
+ * [src_row0, src_row0 + n_rows) of src (slab stride src_row_stride rows) to
+ * rows [dst_row0, dst_row0 + n_rows) of dst (slab stride dst_row_stride rows).
+ * Rows are head_dim elements of dtype.  src and dst must not overlap.
+ */
+int kvs_append_rows(int32_t slabs, int32_t head_dim, int32_t dtype,
+                    const void* src, int64_t src_row_stride, int64_t src_row0,
+                    int64_t n_rows, void* dst, int64_t dst_row_stride, int64_t dst_row0,
+                    void* stream);
+
+/*
+ * Per-kernel timing (tracing).  While enabled, each kernel launch the library
+ * enqueues is bracketed by two HIP events on its stream; kvs_trace_summary
+ * waits for those events and reports, per kernel name, the launch count and
+ * total / min / max duration in milliseconds, then clears the record.  Events
+ * are pooled, so steady-state tracing allocates nothing.  Disabled by default.
+ */
+typedef struct kvs_trace_entry {
+  char name[48];
+  int64_t count;
+  double total_ms;
+  double min_ms;
+  double max_ms;
+} kvs_trace_entry;
+
+int kvs_trace_enable(int on);
+
+/* Writes up to max_entries entries to out (host) and the number of distinct
+ * kernels seen to *n_entries.  Blocks until the recorded events complete. */
+int kvs_trace_summary(kvs_trace_entry* out, int max_entries, int* n_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVS_H_ */

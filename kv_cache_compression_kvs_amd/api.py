@@ -1,0 +1,191 @@
+"""Python binding of the C ABI (include/kvs.h), one function per entry point.
+
+Argument marshalling only: torch tensors become device pointers, host arrays
+become ctypes arrays, the current torch stream becomes the hipStream_t, and a
+nonzero status raises KvsError.  Every step of the computation runs in
+libkvs.so's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Union
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import KVS_BF16, KVS_F32, KvsProblem
+
+Tensorish = Union[torch.Tensor, int, None]
+
+
+class KvsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        text = _lib.lib().kvs_status_string(status).decode()
+        super().__init__(f"{where}: {_lib.STATUS_NAMES.get(status, status)} ({text})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise KvsError(status, where)
+
+
+def _dev(x: Tensorish, name: str) -> Optional[int]:
+    """Device pointer of a contiguous GPU tensor (or a raw int / None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _i64(vals: Optional[Sequence[int]]):
+    if vals is None:
+        return None
+    arr = (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+    return arr
+
+
+def _f64(vals: Optional[Sequence[float]]):
+    if vals is None:
+        return None
+    return (ctypes.c_double * len(vals))(*[float(v) for v in vals])
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return KVS_BF16
+    if t == torch.float32:
+        return KVS_F32
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def make_problem(layers: int, q_heads: int, kv_heads: int, head_dim: int, n_cache: int,
+                 n_sinks: int, chunk_size: int, q_per_chunk: int, dtype: Union[int, torch.dtype],
+                 kv_row_stride: int = 0) -> KvsProblem:
+    if isinstance(dtype, torch.dtype):
+        dtype = dtype_code(dtype)
+    return KvsProblem(layers, q_heads, kv_heads, head_dim, n_cache, n_sinks, chunk_size,
+                      q_per_chunk, kv_row_stride, dtype, 0)
+
+
+# --- entry points, same names as the C ABI -------------------------------------
+
+def kvs_status_string(status: int) -> str:
+    return _lib.lib().kvs_status_string(status).decode()
+
+
+def kvs_version() -> int:
+    return _lib.lib().kvs_version()
+
+
+def kvs_check_problem(p: KvsProblem) -> int:
+    return _lib.lib().kvs_check_problem(ctypes.byref(p))
+
+
+def kvs_num_chunks(p: KvsProblem) -> int:
+    return _lib.lib().kvs_num_chunks(ctypes.byref(p))
+
+
+def kvs_num_queries(p: KvsProblem) -> int:
+    return _lib.lib().kvs_num_queries(ctypes.byref(p))
+
+
+def kvs_workspace_bytes(p: KvsProblem) -> int:
+    return int(_lib.lib().kvs_workspace_bytes(ctypes.byref(p)))
+
+
+def kvs_layer_budgets(layers: int, total: int, sens: Optional[Sequence[float]], alpha: float,
+                      n_cache: int, n_sinks: int) -> np.ndarray:
+    out = (ctypes.c_int64 * layers)()
+    _check(_lib.lib().kvs_layer_budgets(layers, total, _f64(sens), float(alpha), n_cache,
+                                        n_sinks, out), "kvs_layer_budgets")
+    return np.array(out[:], dtype=np.int64)
+
+
+def kvs_score(p: KvsProblem, q: Tensorish, k: Tensorish, scores: Tensorish, ws: Tensorish,
+              ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    _check(_lib.lib().kvs_score(ctypes.byref(p), _dev(q, "q"), _dev(k, "k"),
+                                _dev(scores, "scores"), _dev(ws, "ws"), ws_bytes,
+                                _stream(stream)), "kvs_score")
+
+
+def kvs_select(p: KvsProblem, scores: Tensorish, k_per_layer: Sequence[int], kept: Tensorish,
+               ws: Tensorish = None, ws_bytes: int = 0, stream=None) -> None:
+    _check(_lib.lib().kvs_select(ctypes.byref(p), _dev(scores, "scores"), _i64(k_per_layer),
+                                 _dev(kept, "kept"), _dev(ws, "ws"), ws_bytes, _stream(stream)),
+           "kvs_select")
+
+
+def kvs_compact(p: KvsProblem, k: Tensorish, v: Tensorish, kept: Tensorish,
+                k_per_layer: Sequence[int], k_out: Tensorish, v_out: Tensorish,
+                out_row_stride: int = 0, stream=None) -> None:
+    _check(_lib.lib().kvs_compact(ctypes.byref(p), _dev(k, "k"), _dev(v, "v"), _dev(kept, "kept"),
+                                  _i64(k_per_layer), _dev(k_out, "k_out"), _dev(v_out, "v_out"),
+                                  out_row_stride, _stream(stream)), "kvs_compact")
+
+
+def kvs_compress_block(p: KvsProblem, q: Tensorish, k: Tensorish, v: Tensorish, total_budget: int,
+                       sens: Optional[Sequence[float]], alpha: float, scores: Tensorish,
+                       kept: Tensorish, k_out: Tensorish, v_out: Tensorish,
+                       out_row_stride: int = 0, ws: Tensorish = None,
+                       ws_bytes: Optional[int] = None, stream=None) -> np.ndarray:
+    """Returns the per-layer budgets chosen on the host."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    kl = (ctypes.c_int64 * p.layers)()
+    _check(_lib.lib().kvs_compress_block(
+        ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), total_budget, _f64(sens),
+        float(alpha), _dev(scores, "scores"), _dev(kept, "kept"), _dev(k_out, "k_out"),
+        _dev(v_out, "v_out"), out_row_stride, kl, _dev(ws, "ws"), ws_bytes, _stream(stream)),
+        "kvs_compress_block")
+    return np.array(kl[:], dtype=np.int64)
+
+
+def kvs_append_rows(slabs: int, head_dim: int, dtype: Union[int, torch.dtype], src: Tensorish,
+                    src_row_stride: int, src_row0: int, n_rows: int, dst: Tensorish,
+                    dst_row_stride: int, dst_row0: int, stream=None) -> None:
+    if isinstance(dtype, torch.dtype):
+        dtype = dtype_code(dtype)
+    _check(_lib.lib().kvs_append_rows(slabs, head_dim, dtype, _dev(src, "src"), src_row_stride,
+                                      src_row0, n_rows, _dev(dst, "dst"), dst_row_stride,
+                                      dst_row0, _stream(stream)), "kvs_append_rows")
+
+
+def workspace(p: KvsProblem, device="cuda") -> torch.Tensor:
+    """A workspace tensor of kvs_workspace_bytes(p) bytes (at least 256)."""
+    n = max(kvs_workspace_bytes(p), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def kvs_trace_enable(on: bool) -> None:
+    _check(_lib.lib().kvs_trace_enable(1 if on else 0), "kvs_trace_enable")
+
+
+def kvs_trace_summary() -> dict:
+    """{kernel name: {"count", "total_ms", "min_ms", "max_ms", "avg_ms"}}; clears the record."""
+    cap = 64
+    buf = (_lib.KvsTraceEntry * cap)()
+    n = ctypes.c_int32(0)
+    _check(_lib.lib().kvs_trace_summary(buf, cap, ctypes.byref(n)), "kvs_trace_summary")
+    out = {}
+    for e in buf[:min(n.value, cap)]:
+        out[e.name.decode()] = {"count": e.count, "total_ms": e.total_ms, "min_ms": e.min_ms,
+                                "max_ms": e.max_ms,
+                                "avg_ms": e.total_ms / e.count if e.count else 0.0}
+    return out

@@ -1,0 +1,172 @@
+// Row movers: headwise compaction and block append.
+//
+// Compaction (KV² summary, "전제와 한계": serving needs the cache physically
+// compacted per head): output row t of slab (l, g) is K[l, g, kept[t]] (and
+// the same for V).  Append (EpiCache review, "방법: 3단계" (2), Fig. 1(b)):
+// the next block's rows are copied behind the kept cache.
+//
+// Both are pure HBM streams.  A row is head_dim * element bytes (128-512 B);
+// each lane moves one 16-byte piece, a 256-thread workgroup moves
+// 256 / pieces_per_row rows per pass and four passes per launch slot, with all
+// loads issued before the stores so that eight 16-byte reads per lane
+// (K and V) are in flight.
+#include "kvs_device.h"
+#include "kvs_internal.h"
+#include "kvs_trace.h"
+
+namespace kvs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+struct CompactArgs {
+  const uint8_t* k;
+  const uint8_t* v;
+  const int32_t* kept;
+  uint8_t* ko;
+  uint8_t* vo;
+  int64_t row_bytes, kv_stride, out_stride, n_cache;
+  int32_t Hkv;
+  LayerTable t;
+};
+
+template <int LPR>
+__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
+  constexpr int RPP = kThreads / LPR;
+  const int64_t unit = blockIdx.y;
+  const int64_t l = unit / a.Hkv, g = unit % a.Hkv;
+  const int64_t kl = a.t.k[l];
+  const int64_t t0 = (int64_t)blockIdx.x * (RPP * kUnroll);
+  if (t0 >= kl) return;
+  const int32_t* kp = a.kept + a.t.off[l] + g * kl;
+  const int64_t slab = (l * a.Hkv + g) * a.kv_stride * a.row_bytes;
+  const uint8_t* ks = a.k + slab;
+  const uint8_t* vs = a.v + slab;
+  const int64_t orow0 = a.out_stride ? (l * a.Hkv + g) * a.out_stride : a.t.off[l] + g * kl;
+  uint8_t* ko = a.ko + orow0 * a.row_bytes;
+  uint8_t* vo = a.vo + orow0 * a.row_bytes;
+  const int piece = threadIdx.x % LPR;
+  const int rsub = threadIdx.x / LPR;
+
+  u32x4 kb[kUnroll], vb[kUnroll];
+  bool ok[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t t = t0 + u * RPP + rsub;
+    ok[u] = false;
+    if (t < kl) {
+      const int64_t idx = kp[t];
+      ok[u] = idx >= 0 && idx < a.n_cache;  // rows outside the cache are skipped
+      if (ok[u]) {
+        const int64_t src = idx * a.row_bytes + piece * 16;
+        kb[u] = *(const u32x4*)(ks + src);
+        vb[u] = *(const u32x4*)(vs + src);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t t = t0 + u * RPP + rsub;
+    if (ok[u]) {
+      const int64_t dst = t * a.row_bytes + piece * 16;
+      *(u32x4*)(ko + dst) = kb[u];
+      *(u32x4*)(vo + dst) = vb[u];
+    }
+  }
+}
+
+template <int LPR>
+__global__ __launch_bounds__(kThreads) void append_kernel(const uint8_t* src, int64_t src_stride,
+                                                          int64_t src_row0, int64_t n_rows,
+                                                          uint8_t* dst, int64_t dst_stride,
+                                                          int64_t dst_row0, int64_t row_bytes) {
+  constexpr int RPP = kThreads / LPR;
+  const int64_t slab = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * (RPP * kUnroll);
+  const uint8_t* s = src + (slab * src_stride + src_row0) * row_bytes;
+  uint8_t* d = dst + (slab * dst_stride + dst_row0) * row_bytes;
+  const int piece = threadIdx.x % LPR;
+  const int rsub = threadIdx.x / LPR;
+  u32x4 b[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t t = t0 + u * RPP + rsub;
+    if (t < n_rows) b[u] = *(const u32x4*)(s + t * row_bytes + piece * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t t = t0 + u * RPP + rsub;
+    if (t < n_rows) *(u32x4*)(d + t * row_bytes + piece * 16) = b[u];
+  }
+}
+
+template <int LPR>
+int compact_lpr(const CompactArgs& a, int64_t units, int32_t k_max, hipStream_t st) {
+  constexpr int RPP = kThreads / LPR;
+  const int64_t gx = ceil_div(k_max, RPP * kUnroll);
+  if (gx <= 0 || units <= 0) return 0;
+  TraceScope ts("compact", st);
+  hipLaunchKernelGGL(compact_kernel<LPR>, dim3((unsigned)gx, (unsigned)units), dim3(kThreads), 0,
+                     st, a);
+  return (int)hipGetLastError();
+}
+
+template <int LPR>
+int append_lpr(int32_t slabs, int64_t row_bytes, const void* src, int64_t src_stride,
+               int64_t src_row0, int64_t n_rows, void* dst, int64_t dst_stride,
+               int64_t dst_row0, hipStream_t st) {
+  constexpr int RPP = kThreads / LPR;
+  const int64_t gx = ceil_div(n_rows, RPP * kUnroll);
+  if (gx <= 0 || slabs <= 0) return 0;
+  TraceScope ts("append", st);
+  hipLaunchKernelGGL(append_kernel<LPR>, dim3((unsigned)gx, (unsigned)slabs), dim3(kThreads), 0,
+                     st, static_cast<const uint8_t*>(src), src_stride, src_row0, n_rows,
+                     static_cast<uint8_t*>(dst), dst_stride, dst_row0, row_bytes);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_compact(const kvs_problem& p, const void* k, const void* v, const int32_t* kept,
+                   const LayerTable& t, int32_t k_max, void* k_out, void* v_out,
+                   int64_t out_row_stride, void* stream) {
+  CompactArgs a;
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.kept = kept;
+  a.ko = static_cast<uint8_t*>(k_out);
+  a.vo = static_cast<uint8_t*>(v_out);
+  a.row_bytes = (int64_t)p.head_dim * (p.dtype == KVS_F32 ? 4 : 2);
+  a.kv_stride = p.kv_row_stride ? p.kv_row_stride : p.n_cache;
+  a.out_stride = out_row_stride;
+  a.n_cache = p.n_cache;
+  a.Hkv = p.kv_heads;
+  a.t = t;
+  const int64_t units = (int64_t)p.layers * p.kv_heads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (a.row_bytes) {
+    case 128: return compact_lpr<8>(a, units, k_max, st);
+    case 256: return compact_lpr<16>(a, units, k_max, st);
+    default: return compact_lpr<32>(a, units, k_max, st);
+  }
+}
+
+int launch_append(int32_t slabs, int64_t row_bytes, const void* src, int64_t src_stride,
+                  int64_t src_row0, int64_t n_rows, void* dst, int64_t dst_stride,
+                  int64_t dst_row0, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (row_bytes) {
+    case 128:
+      return append_lpr<8>(slabs, row_bytes, src, src_stride, src_row0, n_rows, dst, dst_stride,
+                           dst_row0, st);
+    case 256:
+      return append_lpr<16>(slabs, row_bytes, src, src_stride, src_row0, n_rows, dst, dst_stride,
+                            dst_row0, st);
+    default:
+      return append_lpr<32>(slabs, row_bytes, src, src_stride, src_row0, n_rows, dst, dst_stride,
+                            dst_row0, st);
+  }
+}
+
+}  // namespace kvs

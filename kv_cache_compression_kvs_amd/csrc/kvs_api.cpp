@@ -1,0 +1,318 @@
+// C ABI of libkvs: argument validation, launch planning, per-layer budgets and
+// dispatch to the HIP launchers.  Pure host C++; every check runs before any
+// work is enqueued, so a rejected call leaves all outputs untouched.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "kvs_internal.h"
+
+namespace kvs {
+namespace {
+
+constexpr int64_t kMaxGrid = 0x7fffffffLL;
+constexpr int kVersion = 10000;  // 1.0.0
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+inline bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+int64_t chunks_of(const kvs_problem& p) {
+  if (p.n_cache <= p.n_sinks) return 0;
+  return cdiv(p.n_cache - p.n_sinks, p.chunk_size);
+}
+
+int check(const kvs_problem* p) {
+  if (!p) return KVS_E_NULL;
+  if (p->layers < 1 || p->layers > KVS_MAX_LAYERS) return KVS_E_SHAPE;
+  if (p->q_heads < 1 || p->kv_heads < 1 || p->q_heads % p->kv_heads) return KVS_E_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return KVS_E_SHAPE;
+  if (p->n_cache < 0 || p->n_cache > INT32_MAX) return KVS_E_SHAPE;
+  if (p->n_sinks < 0 || p->chunk_size < 1 || p->q_per_chunk < 1) return KVS_E_SHAPE;
+  if (p->kv_row_stride != 0 && p->kv_row_stride < p->n_cache) return KVS_E_SHAPE;
+  if (p->dtype != KVS_F32 && p->dtype != KVS_BF16) return KVS_E_DTYPE;
+  if (p->flags != 0) return KVS_E_SHAPE;
+  const int64_t R = chunks_of(*p);
+  const int64_t nq_total = R * p->q_per_chunk;
+  if (R > 0 && nq_total / R != p->q_per_chunk) return KVS_E_SHAPE;
+  const ScorePlan pl = plan_score(*p);
+  // every launch grid must fit the 31-bit x dimension
+  if (p->dtype == KVS_BF16 && pl.units * pl.splits * pl.row_blocks + 8 > kMaxGrid)
+    return KVS_E_SHAPE;
+  if (pl.units * pl.n_chunks * std::max<int64_t>(pl.p2_tiles, 1) + 8 > kMaxGrid) return KVS_E_SHAPE;
+  if (pl.total_rows / 256 + 1 > kMaxGrid) return KVS_E_SHAPE;
+  return KVS_OK;
+}
+
+int to_status(int hip_err) { return hip_err ? KVS_E_HIP : KVS_OK; }
+
+// Largest-remainder split of `total` by sens^alpha (EpiCache review,
+// "+α: 레이어별 예산 배분").  Returns a status; k is written only on success.
+int budgets(int32_t L, int64_t total, const double* sens, double alpha, int64_t n_cache,
+            int64_t n_sinks, int64_t* k) {
+  if (!k) return KVS_E_NULL;
+  if (L < 1 || L > KVS_MAX_LAYERS) return KVS_E_SHAPE;
+  if (total < 0) return KVS_E_BUDGET;
+  std::vector<double> w(L, 1.0);
+  if (sens) {
+    if (!std::isfinite(alpha) || alpha < 0) return KVS_E_BUDGET;
+    for (int l = 0; l < L; ++l) {
+      if (!std::isfinite(sens[l]) || !(sens[l] > 0)) return KVS_E_BUDGET;
+      w[l] = std::pow(sens[l], alpha);
+    }
+  }
+  double sum = 0;
+  for (int l = 0; l < L; ++l) sum += w[l];
+  if (!(sum > 0) || !std::isfinite(sum)) return KVS_E_BUDGET;
+  std::vector<int64_t> base(L);
+  std::vector<double> frac(L);
+  int64_t used = 0;
+  for (int l = 0; l < L; ++l) {
+    const double share = (double)total * w[l] / sum;
+    const double fl = std::floor(share);
+    base[l] = (int64_t)fl;
+    frac[l] = share - fl;
+    used += base[l];
+  }
+  int64_t left = total - used;
+  std::vector<int> order(L);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return frac[a] > frac[b]; });
+  for (int i = 0; i < L && left > 0; ++i, --left) base[order[i]] += 1;
+  if (left != 0) return KVS_E_BUDGET;  // only if rounding drifted by more than L
+  for (int l = 0; l < L; ++l)
+    if (base[l] < n_sinks || base[l] > n_cache) return KVS_E_BUDGET;
+  std::memcpy(k, base.data(), sizeof(int64_t) * L);
+  return KVS_OK;
+}
+
+int build_table(const kvs_problem& p, const int64_t* kpl, bool for_select, int64_t out_stride,
+                LayerTable* t, int32_t* k_max) {
+  if (!kpl) return KVS_E_NULL;
+  const int64_t s_eff = std::min(p.n_sinks, p.n_cache);
+  int64_t off = 0, mx = 0;
+  for (int l = 0; l < p.layers; ++l) {
+    const int64_t kl = kpl[l];
+    if (kl < 0 || kl > p.n_cache) return KVS_E_BUDGET;
+    if (for_select && kl < s_eff) return KVS_E_BUDGET;
+    if (out_stride > 0 && kl > out_stride) return KVS_E_BUDGET;
+    t->k[l] = (int32_t)kl;
+    t->off[l] = off;
+    off += (int64_t)p.kv_heads * kl;
+    mx = std::max(mx, kl);
+  }
+  *k_max = (int32_t)mx;
+  return KVS_OK;
+}
+
+int do_score(const kvs_problem& p, const void* q, const void* k, float* scores, void* ws,
+             size_t ws_bytes) {
+  const ScorePlan pl = plan_score(p);
+  if (p.n_cache > 0 && (!k || !scores)) return KVS_E_NULL;
+  if (pl.n_queries > 0 && !q) return KVS_E_NULL;
+  if (pl.ws_bytes > 0 && !ws) return KVS_E_NULL;
+  if (ws_bytes < pl.ws_bytes) return KVS_E_WORKSPACE;
+  if ((q && !aligned(q, 16)) || (k && !aligned(k, 16)) || (scores && !aligned(scores, 4)) ||
+      (ws && !aligned(ws, 256)))
+    return KVS_E_ALIGN;
+  return KVS_OK;
+}
+
+int enqueue_score(const kvs_problem& p, const void* q, const void* k, float* scores, void* ws,
+                  void* stream) {
+  if (p.n_cache == 0) return KVS_OK;
+  const ScorePlan pl = plan_score(p);
+  if (pl.n_chunks == 0)  // every position is a sink
+    return to_status(launch_fill(scores, (int64_t)p.layers * p.kv_heads * p.n_cache, 1.0f, stream));
+  if (p.dtype == KVS_BF16) return to_status(launch_score_bf16(p, pl, q, k, scores, ws, stream));
+  return to_status(launch_score_f32(p, pl, q, k, scores, ws, stream));
+}
+
+}  // namespace
+
+ScorePlan plan_score(const kvs_problem& p) {
+  ScorePlan pl;
+  const int64_t N = std::max<int64_t>(p.n_cache, 0);
+  const int64_t Hkv = std::max(p.kv_heads, 1);
+  const int64_t G = std::max<int64_t>(p.q_heads / Hkv, 1);
+  pl.n_chunks = chunks_of(p);
+  pl.n_queries = pl.n_chunks * std::max<int64_t>(p.q_per_chunk, 1);
+  pl.rows_per_unit = G * pl.n_queries;
+  pl.total_rows = (int64_t)p.layers * p.q_heads * pl.n_queries;
+  pl.units = (int64_t)p.layers * p.kv_heads;
+  if (pl.n_queries == 0 || N == 0) {
+    pl.row_blocks = 0;
+    pl.splits = 1;
+    pl.keys_per_split = 0;
+    pl.p2_tiles = 0;
+    pl.ws_bytes = 0;
+    return pl;
+  }
+  const int64_t chunk_len = std::min(p.chunk_size, N - std::min(p.n_sinks, N));
+  if (p.dtype == KVS_BF16) {
+    pl.row_blocks = cdiv(pl.rows_per_unit, kP1Rows);
+    const int64_t base = pl.units * pl.row_blocks;
+    const int64_t target = 2048;  // about eight resident workgroups per CU
+    const int64_t by_keys = std::max<int64_t>(1, cdiv(N, 4 * kP1Keys));
+    int64_t splits = std::min<int64_t>({cdiv(target, base), (int64_t)kMaxSplits, by_keys});
+    splits = std::max<int64_t>(splits, 1);
+    pl.keys_per_split = cdiv(cdiv(N, splits), kP1Keys) * kP1Keys;
+    pl.splits = cdiv(N, pl.keys_per_split);
+    pl.p2_tiles = cdiv(chunk_len, kP2Keys);
+  } else {
+    pl.row_blocks = cdiv(pl.total_rows, 256);
+    pl.splits = 1;
+    pl.keys_per_split = N;
+    pl.p2_tiles = cdiv(chunk_len, 256);
+  }
+  size_t off = 0;
+  pl.off_c2 = off;
+  off += round256(sizeof(float) * (size_t)pl.total_rows);
+  pl.off_pm = off;
+  pl.off_pl = off;
+  if (pl.splits > 1) {
+    off += round256(sizeof(float) * (size_t)pl.total_rows * (size_t)pl.splits);
+    pl.off_pl = off;
+    off += round256(sizeof(float) * (size_t)pl.total_rows * (size_t)pl.splits);
+  }
+  pl.ws_bytes = off;
+  return pl;
+}
+
+}  // namespace kvs
+
+using namespace kvs;
+
+extern "C" {
+
+const char* kvs_status_string(int status) {
+  switch (status) {
+    case KVS_OK: return "ok";
+    case KVS_E_NULL: return "a required pointer is NULL";
+    case KVS_E_SHAPE: return "sizes are inconsistent or unsupported";
+    case KVS_E_DTYPE: return "element type is not supported";
+    case KVS_E_BUDGET: return "a budget lies outside [n_sinks, n_cache] or the sensitivities are invalid";
+    case KVS_E_ALIGN: return "a device pointer is not suitably aligned";
+    case KVS_E_WORKSPACE: return "workspace is smaller than kvs_workspace_bytes()";
+    case KVS_E_HIP: return "a HIP launch or runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+int kvs_version(void) { return kVersion; }
+
+int kvs_check_problem(const kvs_problem* p) { return check(p); }
+
+int64_t kvs_num_chunks(const kvs_problem* p) { return check(p) == KVS_OK ? chunks_of(*p) : -1; }
+
+int64_t kvs_num_queries(const kvs_problem* p) {
+  return check(p) == KVS_OK ? chunks_of(*p) * p->q_per_chunk : -1;
+}
+
+size_t kvs_workspace_bytes(const kvs_problem* p) {
+  if (check(p) != KVS_OK) return 0;
+  return plan_score(*p).ws_bytes;
+}
+
+int kvs_layer_budgets(int32_t layers, int64_t total, const double* sens, double alpha,
+                      int64_t n_cache, int64_t n_sinks, int64_t* k_out) {
+  return budgets(layers, total, sens, alpha, n_cache, n_sinks, k_out);
+}
+
+int kvs_score(const kvs_problem* p, const void* q, const void* k, float* scores, void* ws,
+              size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  st = do_score(*p, q, k, scores, ws, ws_bytes);
+  if (st) return st;
+  return enqueue_score(*p, q, k, scores, ws, stream);
+}
+
+int kvs_select(const kvs_problem* p, const float* scores, const int64_t* k_per_layer,
+               int32_t* kept, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check(p);
+  if (st) return st;
+  LayerTable t;
+  int32_t kmax = 0;
+  st = build_table(*p, k_per_layer, true, 0, &t, &kmax);
+  if (st) return st;
+  if (p->n_cache > 0 && (!scores || !kept)) return KVS_E_NULL;
+  if ((scores && !aligned(scores, 4)) || (kept && !aligned(kept, 4))) return KVS_E_ALIGN;
+  return to_status(launch_select(*p, scores, t, kept, stream));
+}
+
+int kvs_compact(const kvs_problem* p, const void* k, const void* v, const int32_t* kept,
+                const int64_t* k_per_layer, void* k_out, void* v_out, int64_t out_row_stride,
+                void* stream) {
+  int st = check(p);
+  if (st) return st;
+  if (out_row_stride < 0) return KVS_E_SHAPE;
+  LayerTable t;
+  int32_t kmax = 0;
+  st = build_table(*p, k_per_layer, false, out_row_stride, &t, &kmax);
+  if (st) return st;
+  if (kmax == 0) return KVS_OK;
+  if (!k || !v || !kept || !k_out || !v_out) return KVS_E_NULL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
+      !aligned(kept, 4))
+    return KVS_E_ALIGN;
+  return to_status(launch_compact(*p, k, v, kept, t, kmax, k_out, v_out, out_row_stride, stream));
+}
+
+int kvs_compress_block(const kvs_problem* p, const void* q, const void* k, const void* v,
+                       int64_t total_budget, const double* sens, double alpha, float* scores,
+                       int32_t* kept, void* k_out, void* v_out, int64_t out_row_stride,
+                       int64_t* k_per_layer_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  if (out_row_stride < 0) return KVS_E_SHAPE;
+  std::vector<int64_t> kl(p->layers);
+  if (total_budget >= (int64_t)p->layers * p->n_cache) {
+    std::fill(kl.begin(), kl.end(), p->n_cache);  // everything fits: copy through
+  } else {
+    st = budgets(p->layers, total_budget, sens, alpha, p->n_cache, p->n_sinks, kl.data());
+    if (st) return st;
+  }
+  LayerTable t;
+  int32_t kmax = 0;
+  st = build_table(*p, kl.data(), true, out_row_stride, &t, &kmax);
+  if (st) return st;
+  st = do_score(*p, q, k, scores, ws, ws_bytes);
+  if (st) return st;
+  if (p->n_cache > 0 && (!kept || !v || !k_out || !v_out)) return KVS_E_NULL;
+  if ((kept && !aligned(kept, 4)) || (v && !aligned(v, 16)) || (k_out && !aligned(k_out, 16)) ||
+      (v_out && !aligned(v_out, 16)))
+    return KVS_E_ALIGN;
+  if (k_per_layer_out) std::memcpy(k_per_layer_out, kl.data(), sizeof(int64_t) * p->layers);
+  if (p->n_cache == 0) return KVS_OK;
+  st = enqueue_score(*p, q, k, scores, ws, stream);
+  if (st) return st;
+  st = to_status(launch_select(*p, scores, t, kept, stream));
+  if (st) return st;
+  if (kmax == 0) return KVS_OK;
+  return to_status(launch_compact(*p, k, v, kept, t, kmax, k_out, v_out, out_row_stride, stream));
+}
+
+int kvs_append_rows(int32_t slabs, int32_t head_dim, int32_t dtype, const void* src,
+                    int64_t src_row_stride, int64_t src_row0, int64_t n_rows, void* dst,
+                    int64_t dst_row_stride, int64_t dst_row0, void* stream) {
+  if (slabs < 0 || n_rows < 0 || src_row0 < 0 || dst_row0 < 0) return KVS_E_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return KVS_E_SHAPE;
+  if (dtype != KVS_F32 && dtype != KVS_BF16) return KVS_E_DTYPE;
+  if (src_row0 + n_rows > src_row_stride || dst_row0 + n_rows > dst_row_stride) return KVS_E_SHAPE;
+  if (slabs == 0 || n_rows == 0) return KVS_OK;
+  if (!src || !dst) return KVS_E_NULL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return KVS_E_ALIGN;
+  const int64_t row_bytes = (int64_t)head_dim * (dtype == KVS_F32 ? 4 : 2);
+  if (cdiv(n_rows, 64) > kMaxGrid) return KVS_E_SHAPE;
+  return to_status(launch_append(slabs, row_bytes, src, src_row_stride, src_row0, n_rows, dst,
+                                 dst_row_stride, dst_row0, stream));
+}
+
+}  // extern "C"

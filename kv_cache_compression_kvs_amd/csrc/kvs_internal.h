@@ -1,0 +1,59 @@
+// Internal interface between the C ABI layer (kvs_api.cpp, pure host C++) and
+// the HIP launchers (*.hip).  Nothing here is exported.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/kvs.h"
+
+namespace kvs {
+
+// Launch geometry and workspace layout of one kvs_score call.  Computed on the
+// host from the problem alone, so kvs_workspace_bytes and kvs_score agree.
+struct ScorePlan {
+  int64_t n_chunks = 0;       // R
+  int64_t n_queries = 0;      // Nq = R * nq
+  int64_t rows_per_unit = 0;  // G * Nq: the query rows that read one KV head
+  int64_t total_rows = 0;     // L * Hq * Nq
+  int64_t units = 0;          // L * Hkv
+  int64_t row_blocks = 0;     // pass-1 workgroups along the rows of a unit
+  int64_t splits = 1;         // pass-1 workgroups along the keys
+  int64_t keys_per_split = 0; // multiple of the pass-1 key tile
+  int64_t p2_tiles = 0;       // pass-2 key tiles per chunk
+  size_t off_c2 = 0;          // workspace offsets (bytes)
+  size_t off_pm = 0;
+  size_t off_pl = 0;
+  size_t ws_bytes = 0;
+};
+
+// Per-layer budget table carried in kernel arguments.
+struct LayerTable {
+  int32_t k[KVS_MAX_LAYERS];     // kept rows per (layer, KV head)
+  int64_t off[KVS_MAX_LAYERS];   // Hkv * sum_{l' < l} k[l']
+};
+
+ScorePlan plan_score(const kvs_problem& p);
+
+// Launchers.  Each returns 0 on success or a nonzero HIP error code.
+int launch_score_bf16(const kvs_problem& p, const ScorePlan& pl, const void* q,
+                      const void* k, float* scores, void* ws, void* stream);
+int launch_score_f32(const kvs_problem& p, const ScorePlan& pl, const void* q,
+                     const void* k, float* scores, void* ws, void* stream);
+int launch_fill(float* dst, int64_t n, float value, void* stream);
+int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t,
+                  int32_t* kept, void* stream);
+int launch_compact(const kvs_problem& p, const void* k, const void* v, const int32_t* kept,
+                   const LayerTable& t, int32_t k_max, void* k_out, void* v_out,
+                   int64_t out_row_stride, void* stream);
+int launch_append(int32_t slabs, int64_t row_bytes, const void* src, int64_t src_stride,
+                  int64_t src_row0, int64_t n_rows, void* dst, int64_t dst_stride,
+                  int64_t dst_row0, void* stream);
+
+// Pass-1 tiling constants shared by the planner and the kernels.
+constexpr int kP1Rows = 256;      // query rows per pass-1 workgroup (4 waves x 64)
+constexpr int kP1Keys = 64;       // keys per pass-1 LDS tile
+constexpr int kP2Keys = 256;      // keys per pass-2 workgroup (4 waves x 64)
+constexpr int kMaxSplits = 64;
+
+}  // namespace kvs

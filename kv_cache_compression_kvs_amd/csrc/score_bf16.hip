@@ -1,0 +1,401 @@
+// Attention scoring of appended queries over a bf16 cache, on bf16 MFMA.
+//
+// What is computed (KV² summary, "무엇과 다른가"): for every query row j of a
+// query head h and every cached key i, z_ji = q_j . k_i / sqrt(d); the
+// probability p_ji = exp(z_ji) / sum_i' exp(z_ji') is normalised over the whole
+// cache; a position i of chunk C_r scores max over the heads sharing its KV
+// head and over C_r's rows of p_ji.  Sinks score 1.
+//
+// Two passes, everything in base-2 units (c1 = log2(e) / sqrt(d)):
+//   pass 1  c2_j = log2 sum_i 2^(z_ji c1): a running max and sum per row over
+//           all N keys (optionally split along the keys and merged after).
+//           The score matrix is formed transposed, keys x queries, so each
+//           lane owns one query and its keys sit in its own registers: the row
+//           reduction needs no cross-lane traffic inside the key loop.
+//   pass 2  score_i = 2^(max_j (z_ji c1 - c2_j)), the max taken over the rows
+//           of the chunk that owns i.  Formed queries x keys so each lane owns
+//           one key; -c2_j / c1 is preloaded into the accumulator, so the hot
+//           loop is MFMA plus one running max per element, and a single exp2
+//           per position at the end (max of exp = exp of max).
+//
+// Pass 1 workgroup: 4 waves x 64 query rows (two 32-column MFMA blocks per
+// wave, Q fragments resident in VGPRs); keys stream through a double-buffered
+// LDS tile of 64 rows padded by 16 bytes per row (conflict-free 16-byte reads).
+// Pass 2 workgroup: 4 waves x 64 keys resident in VGPRs; the chunk's query
+// rows (all heads of the group) stream through LDS in tiles of 64 rows
+// together with their c2 values.
+#include <math.h>
+
+#include "kvs_device.h"
+#include "kvs_internal.h"
+#include "kvs_trace.h"
+
+namespace kvs {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct P1Args {
+  const uint16_t* q;
+  const uint16_t* k;
+  float* c2;        // [total_rows], written when splits == 1
+  float* part_m;    // [splits][total_rows]
+  float* part_l;    // [splits][total_rows]
+  int64_t Nq, N, kv_stride, rows_per_unit, row_blocks, splits, keys_per_split, total_rows;
+  int64_t n_logical;
+  int32_t Hq, Hkv, G;
+  float c1;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
+  constexpr int KS = D / 16;                          // MFMA steps along d
+  constexpr int PIECES = D / 8;                       // 16-byte pieces per row
+  constexpr int LOADS = kP1Keys * PIECES / kThreads;  // pieces per thread per tile
+  constexpr int LD = D + 8;                           // padded LDS row (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kP1Keys * LD];
+
+  const int64_t tau = xcd_remap(blockIdx.x, gridDim.x);
+  if (tau >= a.n_logical) return;
+  const int64_t rb = tau % a.row_blocks;
+  const int64_t t2 = tau / a.row_blocks;
+  const int64_t split = t2 % a.splits;
+  const int64_t unit = t2 / a.splits;
+  const int64_t l = unit / a.Hkv, g = unit % a.Hkv;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+
+  const int64_t unit_row0 = (l * a.Hq + g * a.G) * a.Nq;
+  const uint16_t* qunit = a.q + unit_row0 * D;
+  const uint16_t* kslab = a.k + (l * a.Hkv + g) * a.kv_stride * D;
+  const int64_t row_w = rb * kP1Rows + wave * 64;
+
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    int64_t r = row_w + qb * 32 + col;
+    if (r > a.rows_per_unit - 1) r = a.rows_per_unit - 1;
+    const uint16_t* src = qunit + r * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *(const bf16x8*)(src + ks * 16);
+  }
+
+  const int64_t kbeg = split * a.keys_per_split;
+  const int64_t kend = min(kbeg + a.keys_per_split, a.N);
+  const int64_t ntiles = ceil_div(kend - kbeg, kP1Keys);
+
+  float m[2] = {-INFINITY, -INFINITY};
+  float ls[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const float c1 = a.c1;
+
+  u32x4 pre[LOADS];
+  auto gload = [&](int64_t tile) {
+    const int64_t base = kbeg + tile * kP1Keys;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + i * kThreads;
+      int64_t key = base + c / PIECES;
+      if (key > a.N - 1) key = a.N - 1;  // clamped rows are masked below
+      pre[i] = *(const u32x4*)(kslab + key * D + (c % PIECES) * 8);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + i * kThreads;
+      *(u32x4*)(&sk[buf][(c / PIECES) * LD + (c % PIECES) * 8]) = pre[i];
+    }
+  };
+  auto update = [&](int qb, f32x16 z) {
+    float mx = max3f(max3f(z[0], z[1], z[2]), max3f(z[3], z[4], z[5]), max3f(z[6], z[7], z[8]));
+    mx = max3f(mx, max3f(z[9], z[10], z[11]), max3f(z[12], z[13], z[14]));
+    mx = fmaxf(mx, z[15]);
+    const float mn = fmaxf(m[qb], mx * c1);
+    const float ms = (mn == -INFINITY) ? 0.f : mn;
+    const float sc = exp2_hw(m[qb] - ms);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ls[qb][j] *= sc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ls[qb][i & 3] += exp2_hw(fmaf(z[i], c1, -ms));
+    m[qb] = mn;
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int buf = (int)(t & 1);
+    if (t + 1 < ntiles) gload(t + 1);
+    const int64_t valid = kend - (kbeg + t * kP1Keys);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 acc0 = {}, acc1 = {};
+      const uint16_t* arow = &sk[buf][(kb * 32 + col) * LD + half * 8];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 av = *(const bf16x8*)(arow + ks * 16);
+        acc0 = mfma32x32x16(av, qf[0][ks], acc0);
+        acc1 = mfma32x32x16(av, qf[1][ks], acc1);
+      }
+      if (valid < kP1Keys) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (kb * 32 + acc_row(i, lane) >= valid) {
+            acc0[i] = -INFINITY;
+            acc1[i] = -INFINITY;
+          }
+        }
+      }
+      update(0, acc0);
+      update(1, acc1);
+    }
+    if (t + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lsum = (ls[qb][0] + ls[qb][1]) + (ls[qb][2] + ls[qb][3]);
+    const float mo = swap_halves(m[qb]);
+    const float lo = swap_halves(lsum);
+    const float M = fmaxf(m[qb], mo);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    const float L = lsum * exp2_hw(m[qb] - Ms) + lo * exp2_hw(mo - Ms);
+    const int64_t r = row_w + qb * 32 + col;
+    if (half == 0 && r < a.rows_per_unit) {
+      const int64_t grow = unit_row0 + r;
+      if (a.splits == 1) {
+        a.c2[grow] = M + log2f(L);
+      } else {
+        a.part_m[split * a.total_rows + grow] = M;
+        a.part_l[split * a.total_rows + grow] = L;
+      }
+    }
+  }
+}
+
+// Fixed-order log-sum-exp merge of the per-split partials of pass 1.
+__global__ __launch_bounds__(kThreads) void merge_splits(const float* pm, const float* pl,
+                                                        float* c2, int64_t total_rows,
+                                                        int64_t splits) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= total_rows) return;
+  float M = -INFINITY;
+  for (int64_t s = 0; s < splits; ++s) M = fmaxf(M, pm[s * total_rows + i]);
+  const float Ms = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f;
+  for (int64_t s = 0; s < splits; ++s) L += pl[s * total_rows + i] * exp2_hw(pm[s * total_rows + i] - Ms);
+  c2[i] = M + log2f(L);
+}
+
+struct P2Args {
+  const uint16_t* q;
+  const uint16_t* k;
+  const float* c2;
+  float* scores;
+  int64_t Nq, N, S, m, nq, kv_stride, R, tiles, n_logical;
+  int32_t Hq, Hkv, G;
+  float c1, inv_c1;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void pass2_bf16(P2Args a) {
+  constexpr int KS = D / 16;
+  constexpr int PIECES = D / 8;
+  constexpr int ROWS = 64;
+  constexpr int LOADS = ROWS * PIECES / kThreads;
+  constexpr int LD = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sq[2][ROWS * LD];
+  __shared__ float sc[2][ROWS];
+
+  const int64_t tau = xcd_remap(blockIdx.x, gridDim.x);
+  if (tau >= a.n_logical) return;
+  const int64_t tile = tau % a.tiles;
+  const int64_t t2 = tau / a.tiles;
+  const int64_t r = t2 % a.R;
+  const int64_t unit = t2 / a.R;
+  const int64_t l = unit / a.Hkv, g = unit % a.Hkv;
+  const int64_t c0 = a.S + r * a.m;
+  const int64_t c1e = min(c0 + a.m, a.N);
+  const int64_t kt0 = c0 + tile * kP2Keys;
+  if (kt0 >= c1e) return;  // uniform over the workgroup, before any barrier
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t kw = kt0 + wave * 64;
+  const uint16_t* kslab = a.k + (l * a.Hkv + g) * a.kv_stride * D;
+  float* srow = a.scores + unit * a.N;
+
+  if (r == 0 && tile == 0) {
+    const int64_t ns = min(a.S, a.N);
+    for (int64_t i = tid; i < ns; i += kThreads) srow[i] = 1.0f;
+  }
+
+  bf16x8 kf[2][KS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    int64_t key = kw + kb * 32 + col;
+    if (key > a.N - 1) key = a.N - 1;
+    const uint16_t* src = kslab + key * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *(const bf16x8*)(src + ks * 16);
+  }
+
+  const int64_t unit_row0 = (l * a.Hq + g * a.G) * a.Nq;
+  const uint16_t* qunit = a.q + unit_row0 * D;
+  const int64_t nrows = (int64_t)a.G * a.nq;
+  const int64_t ntiles = ceil_div(nrows, ROWS);
+  float cm[2] = {-INFINITY, -INFINITY};
+
+  u32x4 pre[LOADS];
+  float cpre = INFINITY;
+  auto urow_of = [&](int64_t rho) { return (rho / a.nq) * a.Nq + r * a.nq + (rho % a.nq); };
+  auto gload = [&](int64_t tl) {
+    const int64_t base = tl * ROWS;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + i * kThreads;
+      const int64_t rho = base + c / PIECES;
+      if (rho < nrows) {
+        pre[i] = *(const u32x4*)(qunit + urow_of(rho) * D + (c % PIECES) * 8);
+      } else {
+        pre[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (tid < ROWS) {
+      const int64_t rho = base + tid;
+      cpre = (rho < nrows) ? a.c2[unit_row0 + urow_of(rho)] : INFINITY;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = tid + i * kThreads;
+      *(u32x4*)(&sq[buf][(c / PIECES) * LD + (c % PIECES) * 8]) = pre[i];
+    }
+    if (tid < ROWS) sc[buf][tid] = cpre;
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int buf = (int)(t & 1);
+    if (t + 1 < ntiles) gload(t + 1);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      f32x16 ci;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ci[i] = -sc[buf][rb * 32 + acc_row(i, lane)] * a.inv_c1;
+      const uint16_t* arow = &sq[buf][(rb * 32 + col) * LD + half * 8];
+      f32x16 acc0 = ci, acc1 = ci;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 av = *(const bf16x8*)(arow + ks * 16);
+        acc0 = mfma32x32x16(av, kf[0][ks], acc0);
+        acc1 = mfma32x32x16(av, kf[1][ks], acc1);
+      }
+      float m0 = max3f(max3f(acc0[0], acc0[1], acc0[2]), max3f(acc0[3], acc0[4], acc0[5]),
+                       max3f(acc0[6], acc0[7], acc0[8]));
+      m0 = max3f(m0, max3f(acc0[9], acc0[10], acc0[11]), max3f(acc0[12], acc0[13], acc0[14]));
+      cm[0] = max3f(cm[0], m0, acc0[15]);
+      float m1 = max3f(max3f(acc1[0], acc1[1], acc1[2]), max3f(acc1[3], acc1[4], acc1[5]),
+                       max3f(acc1[6], acc1[7], acc1[8]));
+      m1 = max3f(m1, max3f(acc1[9], acc1[10], acc1[11]), max3f(acc1[12], acc1[13], acc1[14]));
+      cm[1] = max3f(cm[1], m1, acc1[15]);
+    }
+    if (t + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const float v = fmaxf(cm[kb], swap_halves(cm[kb]));
+    const int64_t key = kw + kb * 32 + col;
+    if (half == 0 && key < c1e) srow[key] = fminf(exp2_hw(v * a.c1), 1.0f);
+  }
+}
+
+inline int64_t pad8(int64_t n) { return (n + 7) & ~int64_t(7); }
+
+template <int D>
+int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k, float* scores,
+        void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  float* c2 = reinterpret_cast<float*>(w + pl.off_c2);
+  float* pm = reinterpret_cast<float*>(w + pl.off_pm);
+  float* plw = reinterpret_cast<float*>(w + pl.off_pl);
+  const int64_t N = p.n_cache;
+  const int64_t stride = p.kv_row_stride ? p.kv_row_stride : N;
+  const float c1 = (float)(1.4426950408889634 / sqrt((double)D));
+  const float inv_c1 = (float)(sqrt((double)D) / 1.4426950408889634);
+
+  P1Args a1;
+  a1.q = static_cast<const uint16_t*>(q);
+  a1.k = static_cast<const uint16_t*>(k);
+  a1.c2 = c2;
+  a1.part_m = pm;
+  a1.part_l = plw;
+  a1.Nq = pl.n_queries;
+  a1.N = N;
+  a1.kv_stride = stride;
+  a1.rows_per_unit = pl.rows_per_unit;
+  a1.row_blocks = pl.row_blocks;
+  a1.splits = pl.splits;
+  a1.keys_per_split = pl.keys_per_split;
+  a1.total_rows = pl.total_rows;
+  a1.n_logical = pl.units * pl.splits * pl.row_blocks;
+  a1.Hq = p.q_heads;
+  a1.Hkv = p.kv_heads;
+  a1.G = p.q_heads / p.kv_heads;
+  a1.c1 = c1;
+  {
+    TraceScope ts("score_pass1_bf16", st);
+    hipLaunchKernelGGL(pass1_bf16<D>, dim3((unsigned)pad8(a1.n_logical)), dim3(kThreads), 0, st, a1);
+  }
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  if (pl.splits > 1) {
+    TraceScope ts("score_merge_splits", st);
+    hipLaunchKernelGGL(merge_splits, dim3((unsigned)ceil_div(pl.total_rows, kThreads)),
+                       dim3(kThreads), 0, st, pm, plw, c2, pl.total_rows, pl.splits);
+    if (hipError_t e = hipGetLastError()) return (int)e;
+  }
+
+  P2Args a2;
+  a2.q = a1.q;
+  a2.k = a1.k;
+  a2.c2 = c2;
+  a2.scores = scores;
+  a2.Nq = pl.n_queries;
+  a2.N = N;
+  a2.S = p.n_sinks;
+  a2.m = p.chunk_size;
+  a2.nq = p.q_per_chunk;
+  a2.kv_stride = stride;
+  a2.R = pl.n_chunks;
+  a2.tiles = pl.p2_tiles;
+  a2.n_logical = pl.units * pl.n_chunks * pl.p2_tiles;
+  a2.Hq = p.q_heads;
+  a2.Hkv = p.kv_heads;
+  a2.G = a1.G;
+  a2.c1 = c1;
+  a2.inv_c1 = inv_c1;
+  {
+    TraceScope ts("score_pass2_bf16", st);
+    hipLaunchKernelGGL(pass2_bf16<D>, dim3((unsigned)pad8(a2.n_logical)), dim3(kThreads), 0, st, a2);
+  }
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  return 0;
+}
+
+}  // namespace
+
+int launch_score_bf16(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
+                      float* scores, void* ws, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.head_dim == 128) return run<128>(p, pl, q, k, scores, ws, st);
+  return run<64>(p, pl, q, k, scores, ws, st);
+}
+
+}  // namespace kvs

@@ -1,0 +1,161 @@
+// Attention scoring of appended queries over an fp32 cache (vector ALU).
+//
+// Same two-pass decomposition as the bf16 path (KV² summary, "무엇과 다른가"):
+// pass 1 finds c2_j = log2 sum_i 2^(z_ji c1) for every query row over all N
+// keys; pass 2 takes, for every position i of chunk C_r, the max over the
+// chunk's rows of z_ji c1 - c2_j and exponentiates once.  fp32 inputs keep
+// fp32 arithmetic end to end (a bf16 downcast would cost ~2^-9 relative per
+// logit), so these kernels use fp32 FMAs rather than bf16 MFMA.
+//
+// Pass 1: one thread per query row; all threads of a wave walk the same keys,
+// so key loads are wave-uniform.  Pass 2: one thread per cached position of a
+// chunk; all threads walk the same query rows.
+#include <math.h>
+
+#include "kvs_device.h"
+#include "kvs_internal.h"
+#include "kvs_trace.h"
+
+namespace kvs {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void pass1_f32(const float* __restrict__ q,
+                                                      const float* __restrict__ k,
+                                                      float* __restrict__ c2, int64_t total_rows,
+                                                      int64_t Nq, int64_t N, int64_t kv_stride,
+                                                      int32_t Hq, int32_t Hkv, float c1) {
+  const int64_t row = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t rr = row < total_rows ? row : total_rows - 1;
+  const int64_t h_all = rr / Nq;                 // l * Hq + h
+  const int64_t l = h_all / Hq, h = h_all % Hq;
+  const int64_t g = h / (Hq / Hkv);
+  const float* qr = q + rr * D;
+  const float* ks = k + (l * Hkv + g) * kv_stride * D;
+  float qv[D];
+#pragma unroll
+  for (int t = 0; t < D; ++t) qv[t] = qr[t];
+  float m = -INFINITY, s = 0.f;
+  for (int64_t i = 0; i < N; ++i) {
+    const float* kr = ks + i * D;
+    float z0 = 0.f, z1 = 0.f, z2 = 0.f, z3 = 0.f;
+#pragma unroll
+    for (int t = 0; t < D; t += 4) {
+      z0 = fmaf(qv[t], kr[t], z0);
+      z1 = fmaf(qv[t + 1], kr[t + 1], z1);
+      z2 = fmaf(qv[t + 2], kr[t + 2], z2);
+      z3 = fmaf(qv[t + 3], kr[t + 3], z3);
+    }
+    const float z = ((z0 + z1) + (z2 + z3)) * c1;
+    if (z > m) {
+      s = s * exp2_hw(m - z) + 1.f;
+      m = z;
+    } else {
+      s += exp2_hw(z - m);
+    }
+  }
+  if (row < total_rows) c2[row] = m + log2f(s);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void pass2_f32(const float* __restrict__ q,
+                                                      const float* __restrict__ k,
+                                                      const float* __restrict__ c2,
+                                                      float* __restrict__ scores, int64_t Nq,
+                                                      int64_t N, int64_t S, int64_t m_chunk,
+                                                      int64_t nq, int64_t kv_stride, int64_t R,
+                                                      int64_t tiles, int32_t Hq, int32_t Hkv,
+                                                      float c1) {
+  const int64_t b = blockIdx.x;
+  const int64_t tile = b % tiles;
+  const int64_t r = (b / tiles) % R;
+  const int64_t unit = b / (tiles * R);
+  const int64_t l = unit / Hkv, g = unit % Hkv;
+  const int32_t G = Hq / Hkv;
+  const int64_t c0 = S + r * m_chunk;
+  const int64_t c1e = min(c0 + m_chunk, N);
+  float* srow = scores + unit * N;
+  if (r == 0 && tile == 0) {
+    const int64_t ns = min(S, N);
+    for (int64_t i = threadIdx.x; i < ns; i += kThreads) srow[i] = 1.0f;
+  }
+  const int64_t key = c0 + tile * kThreads + threadIdx.x;
+  if (key >= c1e) return;
+  const float* kr = k + ((l * Hkv + g) * kv_stride + key) * D;
+  float kv[D];
+#pragma unroll
+  for (int t = 0; t < D; ++t) kv[t] = kr[t];
+  const int64_t unit_row0 = (l * Hq + g * G) * Nq;
+  float best = -INFINITY;
+  for (int32_t hh = 0; hh < G; ++hh) {
+    for (int64_t j = 0; j < nq; ++j) {
+      const int64_t row = unit_row0 + hh * Nq + r * nq + j;
+      const float* qr = q + row * D;
+      float z0 = 0.f, z1 = 0.f, z2 = 0.f, z3 = 0.f;
+#pragma unroll
+      for (int t = 0; t < D; t += 4) {
+        z0 = fmaf(qr[t], kv[t], z0);
+        z1 = fmaf(qr[t + 1], kv[t + 1], z1);
+        z2 = fmaf(qr[t + 2], kv[t + 2], z2);
+        z3 = fmaf(qr[t + 3], kv[t + 3], z3);
+      }
+      const float z = ((z0 + z1) + (z2 + z3)) * c1;
+      best = fmaxf(best, z - c2[row]);
+    }
+  }
+  srow[key] = fminf(exp2_hw(best), 1.0f);
+}
+
+template <int D>
+int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k, float* scores,
+        void* ws, hipStream_t st) {
+  float* c2 = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_c2);
+  const int64_t N = p.n_cache;
+  const int64_t stride = p.kv_row_stride ? p.kv_row_stride : N;
+  const float c1 = (float)(1.4426950408889634 / sqrt((double)D));
+  const float* qf = static_cast<const float*>(q);
+  const float* kf = static_cast<const float*>(k);
+  {
+  TraceScope t1("score_pass1_f32", st);
+  hipLaunchKernelGGL(pass1_f32<D>, dim3((unsigned)ceil_div(pl.total_rows, kThreads)),
+                     dim3(kThreads), 0, st, qf, kf, c2, pl.total_rows, pl.n_queries, N, stride,
+                     p.q_heads, p.kv_heads, c1);
+  }
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  const int64_t tiles = ceil_div(p.chunk_size < N ? p.chunk_size : N, kThreads);
+  {
+  TraceScope t2("score_pass2_f32", st);
+  hipLaunchKernelGGL(pass2_f32<D>, dim3((unsigned)(pl.units * pl.n_chunks * tiles)),
+                     dim3(kThreads), 0, st, qf, kf, c2, scores, pl.n_queries, N, p.n_sinks,
+                     p.chunk_size, p.q_per_chunk, stride, pl.n_chunks, tiles, p.q_heads,
+                     p.kv_heads, c1);
+  }
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  return 0;
+}
+
+__global__ __launch_bounds__(kThreads) void fill_kernel(float* dst, int64_t n, float value) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) dst[i] = value;
+}
+
+}  // namespace
+
+int launch_score_f32(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
+                     float* scores, void* ws, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.head_dim == 128) return run<128>(p, pl, q, k, scores, ws, st);
+  return run<64>(p, pl, q, k, scores, ws, st);
+}
+
+int launch_fill(float* dst, int64_t n, float value, void* stream) {
+  if (n <= 0) return 0;
+  TraceScope ts("fill", static_cast<hipStream_t>(stream));
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)ceil_div(n, kThreads)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), dst, n, value);
+  return (int)hipGetLastError();
+}
+
+}  // namespace kvs

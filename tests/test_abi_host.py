@@ -1,0 +1,203 @@
+"""The C ABI on the host: the library loads, exports what include/kvs.h declares,
+and its host-only logic (validation, planning, budgets) behaves.  No kernel is
+launched: every device entry point is only called with arguments that fail
+validation before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvs.h")
+
+
+@pytest.fixture(scope="module")
+def K():
+    import kv_cache_compression_kvs_amd as pkg
+    if not os.path.exists(pkg.LIB_PATH):
+        from kv_cache_compression_kvs_amd import build
+        build.build()
+    return pkg
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvs_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(K):
+    from kv_cache_compression_kvs_amd import _lib
+    names = declared_functions()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (kvs_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert n in _lib.SIGNATURES, n
+    h = _lib.lib()
+    for n in names:
+        assert getattr(h, n) is not None
+
+
+def test_status_strings_and_version(K):
+    assert K.kvs_status_string(0) == "ok"
+    for s in range(1, 8):
+        assert K.kvs_status_string(s) and K.kvs_status_string(s) != "unknown status"
+    assert K.kvs_status_string(99) == "unknown status"
+    assert K.kvs_version() >= 10000
+
+
+def prob(K, **kw):
+    base = dict(layers=2, q_heads=8, kv_heads=2, head_dim=128, n_cache=4300, n_sinks=4,
+                chunk_size=1024, q_per_chunk=41, dtype=K.KVS_BF16)
+    base.update(kw)
+    return K.make_problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(layers=0), 2), (dict(layers=257), 2),
+    (dict(q_heads=6, kv_heads=4), 2),
+    (dict(head_dim=96), 2),
+    (dict(n_cache=-1), 2),
+    (dict(chunk_size=0), 2), (dict(q_per_chunk=0), 2), (dict(n_sinks=-2), 2),
+    (dict(kv_row_stride=100), 2),
+    (dict(dtype=7), 3),
+    (dict(n_cache=0), 0), (dict(n_cache=3), 0), (dict(head_dim=64, dtype=0), 0),
+])
+def test_check_problem(K, kw, status):
+    assert K.kvs_check_problem(prob(K, **kw)) == status
+
+
+def test_chunk_and_query_counts(K):
+    p = prob(K)
+    assert K.kvs_num_chunks(p) == len(O.chunk_bounds(4300, 4, 1024)) == 5
+    assert K.kvs_num_queries(p) == 5 * 41
+    assert K.kvs_num_chunks(prob(K, n_cache=4)) == 0
+    p = prob(K, layers=36, q_heads=32, kv_heads=8, n_cache=131072, chunk_size=4096, q_per_chunk=410)
+    assert K.kvs_num_chunks(p) == 32 and K.kvs_num_queries(p) == 13120
+
+
+def test_workspace_bytes(K):
+    p = prob(K)
+    ws = K.kvs_workspace_bytes(p)
+    rows = 2 * 8 * 5 * 41
+    assert ws >= rows * 4 and ws % 256 == 0
+    assert K.kvs_workspace_bytes(prob(K, layers=0)) == 0
+    assert K.kvs_workspace_bytes(prob(K, n_cache=3)) == 0
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_budgets_match_oracle(K, seed):
+    rng = np.random.default_rng(seed)
+    L = int(rng.integers(1, 60))
+    T = int(rng.integers(0, 300_000))
+    alpha = float(rng.choice([0.0, 1.0, 2.0, 3.0, 4.0, 8.0, rng.uniform(0, 6)]))
+    sens = rng.uniform(0.5, 1.5, size=L) if seed % 4 else None
+    want = O.layer_budgets(T, L, sens, alpha)
+    got = K.kvs_layer_budgets(L, T, sens, alpha, 1 << 40, 0)
+    assert got.tolist() == want.tolist()
+
+
+def test_budgets_for_the_episodic_workload(K):
+    from workloads import FULL, gen
+    w = FULL["episodic"]
+    sens = gen.sensitivities(w)
+    got = K.kvs_layer_budgets(28, w.total_budget, sens, w.alpha, w.shape.n_cache, 4)
+    want = O.layer_budgets(w.total_budget, 28, sens, w.alpha, n_cache=w.shape.n_cache, n_sinks=4)
+    assert got.tolist() == want.tolist() and int(got.sum()) == 229376
+
+
+def test_budget_errors(K):
+    with pytest.raises(K.KvsError) as e:
+        K.kvs_layer_budgets(2, 10, [1.0, -1.0], 1.0, 100, 0)
+    assert e.value.status == 4
+    with pytest.raises(K.KvsError):
+        K.kvs_layer_budgets(2, 10, [1.0, float("nan")], 1.0, 100, 0)
+    with pytest.raises(K.KvsError):
+        K.kvs_layer_budgets(2, 10, [1.0, 2.0], -0.5, 100, 0)
+    with pytest.raises(K.KvsError):
+        K.kvs_layer_budgets(2, 10, None, 0.0, 4, 0)        # 5 per layer > N
+    with pytest.raises(K.KvsError):
+        K.kvs_layer_budgets(2, 6, None, 0.0, 100, 4)       # 3 per layer < S
+    with pytest.raises(K.KvsError) as e:
+        K.kvs_layer_budgets(0, 6, None, 0.0, 100, 4)
+    assert e.value.status == 2
+
+
+# --- device entry points: only argument errors, nothing is enqueued -----------
+
+FAKE = 1 << 20          # a 16-byte aligned non-null address that is never dereferenced
+
+
+def raw(K):
+    from kv_cache_compression_kvs_amd import _lib
+    return _lib.lib()
+
+
+def test_score_rejects_bad_arguments(K):
+    h = raw(K)
+    p = prob(K)
+    ws = K.kvs_workspace_bytes(p)
+    assert h.kvs_score(None, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
+    assert h.kvs_score(ctypes.byref(p), None, FAKE, FAKE, FAKE, ws, None) == 1
+    assert h.kvs_score(ctypes.byref(p), FAKE, None, FAKE, FAKE, ws, None) == 1
+    assert h.kvs_score(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ws - 1, None) == 6
+    assert h.kvs_score(ctypes.byref(p), FAKE + 2, FAKE, FAKE, FAKE, ws, None) == 5
+    assert h.kvs_score(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE + 16, ws, None) == 5
+    bad = prob(K, head_dim=80)
+    assert h.kvs_score(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, ws, None) == 2
+
+
+def test_select_and_compact_reject_bad_budgets(K):
+    h = raw(K)
+    p = prob(K)
+    ks = (ctypes.c_int64 * 2)(3, 100)       # 3 < S=4
+    assert h.kvs_select(ctypes.byref(p), FAKE, ks, FAKE, None, 0, None) == 4
+    ks = (ctypes.c_int64 * 2)(100, 4301)    # > N
+    assert h.kvs_select(ctypes.byref(p), FAKE, ks, FAKE, None, 0, None) == 4
+    assert h.kvs_select(ctypes.byref(p), FAKE, None, FAKE, None, 0, None) == 1
+    ks = (ctypes.c_int64 * 2)(100, 200)
+    assert h.kvs_select(ctypes.byref(p), None, ks, FAKE, None, 0, None) == 1
+    assert h.kvs_compact(ctypes.byref(p), FAKE, FAKE, FAKE, ks, FAKE, FAKE, 150, None) == 4
+    assert h.kvs_compact(ctypes.byref(p), FAKE, FAKE, FAKE, ks, FAKE, FAKE, -1, None) == 2
+    assert h.kvs_compact(ctypes.byref(p), FAKE, None, FAKE, ks, FAKE, FAKE, 0, None) == 1
+    assert h.kvs_compact(ctypes.byref(p), FAKE, FAKE, FAKE, ks, FAKE + 4, FAKE, 0, None) == 5
+
+
+def test_compress_block_rejects_infeasible_budget(K):
+    h = raw(K)
+    p = prob(K)
+    ws = K.kvs_workspace_bytes(p)
+    kl = (ctypes.c_int64 * 2)(-7, -7)
+    sens = (ctypes.c_double * 2)(1.0, 1.0)
+    # total 6 split over 2 layers gives 3 < S = 4
+    st = h.kvs_compress_block(ctypes.byref(p), FAKE, FAKE, FAKE, 6, sens, 1.0, FAKE, FAKE, FAKE,
+                              FAKE, 0, kl, FAKE, ws, None)
+    assert st == 4 and list(kl) == [-7, -7]
+    sens = (ctypes.c_double * 2)(1.0, 0.0)
+    st = h.kvs_compress_block(ctypes.byref(p), FAKE, FAKE, FAKE, 100, sens, 1.0, FAKE, FAKE, FAKE,
+                              FAKE, 0, kl, FAKE, ws, None)
+    assert st == 4
+    st = h.kvs_compress_block(ctypes.byref(p), FAKE, FAKE, FAKE, 100, None, 0.0, FAKE, FAKE, FAKE,
+                              FAKE, 0, kl, FAKE, 0, None)
+    assert st == 6
+
+
+def test_append_rejects_bad_ranges(K):
+    h = raw(K)
+    assert h.kvs_append_rows(4, 128, 1, FAKE, 100, 90, 20, FAKE, 200, 0, None) == 2
+    assert h.kvs_append_rows(4, 128, 1, FAKE, 100, 0, 20, FAKE, 200, 190, None) == 2
+    assert h.kvs_append_rows(4, 96, 1, FAKE, 100, 0, 20, FAKE, 200, 0, None) == 2
+    assert h.kvs_append_rows(4, 128, 5, FAKE, 100, 0, 20, FAKE, 200, 0, None) == 3
+    assert h.kvs_append_rows(4, 128, 1, None, 100, 0, 20, FAKE, 200, 0, None) == 1
+    assert h.kvs_append_rows(4, 128, 1, FAKE + 8, 100, 0, 20, FAKE, 200, 0, None) == 5
+    assert h.kvs_append_rows(4, 128, 1, None, 100, 0, 0, None, 200, 0, None) == 0  # nothing to do

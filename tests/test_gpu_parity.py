@@ -1,0 +1,349 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Sizes here are ones the oracle finishes in seconds while still spanning several
+kernel tiles and ragged tails; the full workload sizes are in
+test_gpu_full.py.  Every input comes from the seeded generators; every
+expected value comes from the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from workloads import SMALL, ScoreShape, Workload, gen
+
+from gpu_util import assert_kept_match, assert_scores_close, f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import kv_cache_compression_kvs_amd as pkg
+    return pkg
+
+
+def run_score(K, shape: ScoreShape, q, k, poison=True):
+    p = K.make_problem(shape.layers, shape.q_heads, shape.kv_heads, shape.head_dim,
+                       shape.n_cache, shape.n_sinks, shape.chunk_size, shape.q_per_chunk, q.dtype)
+    qd, kd = q.cuda(), k.cuda()
+    scores = torch.full((shape.layers, shape.kv_heads, shape.n_cache), float("nan"),
+                        device="cuda") if poison else torch.empty(
+        (shape.layers, shape.kv_heads, shape.n_cache), device="cuda")
+    ws = K.workspace(p)
+    K.kvs_score(p, qd, kd, scores, ws)
+    torch.cuda.synchronize()
+    return scores
+
+
+def oracle_scores(shape, q, k):
+    return O.scores(f64(q), f64(k), shape.n_sinks, shape.chunk_size, shape.q_per_chunk)
+
+
+# --- scores --------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "kv2_32k", "kv2_131k"])
+def test_score_small_workloads(K, name):
+    w = SMALL[name]
+    x = gen.single_inputs(w)
+    g = run_score(K, w.shape, x["q"], x["k"])
+    o = oracle_scores(w.shape, x["q"], x["k"])
+    worst = assert_scores_close(f64(g), o, name)
+    print(f"{name}: max rel err {worst:.2e}")
+
+
+def test_score_small_episodes(K):
+    w = SMALL["episodic"]
+    x = gen.episodic_inputs(w)
+    for e in range(w.episodes):
+        g = run_score(K, w.shape, x["q_episodes"][e], x["k"])
+        o = oracle_scores(w.shape, x["q_episodes"][e], x["k"])
+        assert_scores_close(f64(g), o, f"episode {e}")
+
+
+EDGE = [
+    # (layers, Hq, Hkv, d, N, S, m, nq, dtype)
+    (1, 1, 1, 128, 1, 0, 1, 1, "bf16"),          # one position, one query
+    (1, 2, 1, 128, 5, 4, 3, 1, "bf16"),          # one non-sink position
+    (1, 4, 4, 128, 300, 0, 300, 3, "bf16"),      # G = 1, no sinks
+    (2, 6, 2, 128, 777, 3, 100, 1, "bf16"),      # nq = 1, ragged chunks
+    (1, 8, 2, 64, 1500, 4, 512, 37, "bf16"),     # d = 64
+    (1, 3, 1, 128, 130, 2, 1, 2, "bf16"),        # chunks of a single position
+    (1, 12, 3, 128, 2049, 4, 2045, 300, "bf16"), # G = 4, rows spill into a second row block
+    (1, 4, 2, 128, 4, 4, 16, 5, "bf16"),         # every position a sink
+    (1, 4, 2, 128, 6, 10, 16, 5, "bf16"),        # N < S
+    (1, 2, 1, 64, 999, 1, 400, 9, "f32"),        # fp32, d = 64, ragged
+    (2, 4, 2, 128, 700, 4, 333, 20, "f32"),      # fp32, d = 128
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[str(c) for c in EDGE])
+def test_score_edge_shapes(K, case):
+    L, Hq, Hkv, d, N, S, m, nq, dt = case
+    shape = ScoreShape(L, Hq, Hkv, d, N, S, m, nq, dt)
+    torch.manual_seed(hash(case) & 0xffff)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    q = (torch.randn(L, Hq, shape.n_queries, d) * 2.0).to(tdt)
+    k = (torch.randn(L, Hkv, N, d) * 2.0).to(tdt)
+    g = run_score(K, shape, q, k)
+    o = oracle_scores(shape, q, k)
+    assert_scores_close(f64(g), o, str(case))
+    assert torch.all(g[..., :min(S, N)] == 1.0)
+
+
+def test_score_large_logits_and_outliers(K):
+    # logits of order 100 and one dominant key per query: exp underflow everywhere else
+    shape = ScoreShape(1, 4, 2, 128, 1000, 4, 400, 16, "bf16")
+    torch.manual_seed(7)
+    k = torch.randn(1, 2, 1000, 128) * 3
+    k[..., 5] += 40.0
+    q = torch.randn(1, 4, shape.n_queries, 128) * 3
+    q[..., 5] += 10.0
+    q, k = q.bfloat16(), k.bfloat16()
+    g = run_score(K, shape, q, k)
+    assert_scores_close(f64(g), oracle_scores(shape, q, k), "large logits")
+
+
+def test_score_is_deterministic(K):
+    w = SMALL["kv2_32k"]
+    x = gen.single_inputs(w)
+    a = run_score(K, w.shape, x["q"], x["k"])
+    b = run_score(K, w.shape, x["q"], x["k"], poison=False)
+    assert torch.equal(a, b)
+
+
+# --- selection ------------------------------------------------------------------
+
+SEL = [
+    # (units_per_layer, layers, N, S, kind, ks)
+    (2, 2, 300, 4, "uniform", [4, 150]),
+    (2, 1, 300, 4, "coarse", [100]),
+    (3, 1, 1000, 0, "equal", [0]),
+    (3, 1, 1000, 0, "equal", [999]),
+    (1, 2, 5000, 4, "sparse", [4, 300]),
+    (2, 1, 6144, 4, "tiny", [4096]),
+    (2, 1, 6144, 4, "coarse", [4096]),
+    (1, 1, 32768, 4, "uniform", [1638]),        # LDS-resident path, largest size
+    (1, 1, 40000, 4, "coarse", [2000]),          # global-memory path
+    (1, 1, 131072, 4, "uniform", [2621]),
+    (1, 1, 131072, 4, "equal", [2621]),
+    (2, 1, 700, 4, "uniform", [700]),            # keep everything
+    (1, 1, 1, 0, "uniform", [1]),
+    (1, 1, 3, 5, "uniform", [3]),                # N < S: all sinks
+]
+
+
+@pytest.mark.parametrize("case", SEL, ids=[str(c) for c in SEL])
+def test_select_matches_oracle_exactly(K, case):
+    Hkv, L, N, S, kind, ks = case
+    scores = gen.score_tensor(L * Hkv, N, S, kind, seed=N + len(ks))
+    p = K.make_problem(L, Hkv, Hkv, 128, N, S, max(N - S, 1), 1, torch.bfloat16)
+    total = Hkv * sum(ks)
+    kept = torch.full((max(total, 1),), -7, dtype=torch.int32, device="cuda")
+    K.kvs_select(p, scores.cuda(), ks, kept)
+    torch.cuda.synchronize()
+    got = kept.cpu().numpy()
+    s64 = scores.double().numpy().reshape(L, Hkv, N)
+    want = O.pack_kept(O.select(s64, ks, S))
+    assert np.array_equal(got[:total], want)
+
+
+# --- compaction and append -----------------------------------------------------
+
+@pytest.mark.parametrize("dt,d,stride", [(torch.bfloat16, 128, 0), (torch.bfloat16, 64, 0),
+                                         (torch.float32, 64, 0), (torch.float32, 128, 0),
+                                         (torch.bfloat16, 128, 900)])
+def test_compact_is_bit_exact(K, dt, d, stride):
+    L, Hkv, N, S = 3, 2, 1234, 4
+    ks = [5, 777, 300]
+    torch.manual_seed(d)
+    k = torch.randn(L, Hkv, N, d).to(dt)
+    v = torch.randn(L, Hkv, N, d).to(dt)
+    kept = gen.kept_lists(Hkv, N, S, ks, seed=d)
+    p = K.make_problem(L, Hkv, Hkv, d, N, S, N, 1, dt)
+    rows = Hkv * sum(ks) if stride == 0 else L * Hkv * stride
+    ko = torch.zeros(rows, d, dtype=dt, device="cuda")
+    vo = torch.zeros(rows, d, dtype=dt, device="cuda")
+    K.kvs_compact(p, k.cuda(), v.cuda(), kept.cuda(), ks, ko, vo, out_row_stride=stride)
+    torch.cuda.synchronize()
+    per = [kept[sum(Hkv * x for x in ks[:l]):sum(Hkv * x for x in ks[:l + 1])].view(Hkv, -1).long().numpy()
+           for l in range(L)]
+    want = O.compact(k.numpy() if dt == torch.float32 else k.view(torch.int16).numpy(),
+                     v.numpy() if dt == torch.float32 else v.view(torch.int16).numpy(), per)
+    ko_c = ko.cpu() if dt == torch.float32 else ko.cpu().view(torch.int16)
+    vo_c = vo.cpu() if dt == torch.float32 else vo.cpu().view(torch.int16)
+    off = 0
+    for l in range(L):
+        for g in range(Hkv):
+            if stride:
+                r0 = (l * Hkv + g) * stride
+            else:
+                r0 = off + g * ks[l]
+            assert np.array_equal(ko_c[r0:r0 + ks[l]].numpy(), want[l][0][g])
+            assert np.array_equal(vo_c[r0:r0 + ks[l]].numpy(), want[l][1][g])
+        off += Hkv * ks[l]
+
+
+def test_append_rows_is_bit_exact(K):
+    slabs, d, T, cap = 6, 128, 1000, 700
+    src = torch.randn(slabs, T, d).bfloat16().cuda()
+    dst = torch.zeros(slabs, cap, d).bfloat16().cuda()
+    K.kvs_append_rows(slabs, d, torch.bfloat16, src, T, 333, 517, dst, cap, 100)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:, 100:617], src[:, 333:850])
+    assert torch.count_nonzero(dst[:, :100].float()) == 0
+    assert torch.count_nonzero(dst[:, 617:].float()) == 0
+
+
+# --- whole compressions -------------------------------------------------------------
+
+def compress_and_check(K, shape: ScoreShape, q, k, v, total, sens=None, alpha=0.0, what=""):
+    p = K.make_problem(shape.layers, shape.q_heads, shape.kv_heads, shape.head_dim,
+                       shape.n_cache, shape.n_sinks, shape.chunk_size, shape.q_per_chunk, q.dtype)
+    L, Hkv, N, d = k.shape
+    kl = O.layer_budgets(total, L, sens, alpha, n_cache=N, n_sinks=shape.n_sinks) \
+        if total < L * N else np.full(L, N)
+    rows = int(Hkv * kl.sum())
+    scores = torch.full((L, Hkv, N), float("nan"), device="cuda")
+    kept = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
+    ko = torch.zeros(rows, d, dtype=k.dtype, device="cuda")
+    vo = torch.zeros(rows, d, dtype=k.dtype, device="cuda")
+    kd, vd = k.cuda(), v.cuda()
+    got_kl = K.kvs_compress_block(p, q.cuda(), kd, vd, total, sens, alpha, scores, kept, ko, vo,
+                                  0, ws=K.workspace(p))
+    torch.cuda.synchronize()
+    assert got_kl.tolist() == kl.tolist()
+    o = oracle_scores(shape, q, k)
+    assert_scores_close(f64(scores), o, what)
+    off = 0
+    diffs = 0
+    for l in range(L):
+        for g in range(Hkv):
+            a = off + g * int(kl[l])
+            kr = kept[a:a + int(kl[l])]
+            diffs += assert_kept_match(kr.cpu().numpy(), o[l, g], int(kl[l]), shape.n_sinks,
+                                       f"{what} l={l} g={g}")
+            idx = kr.long()
+            assert torch.equal(ko[a:a + int(kl[l])], kd[l, g, idx])
+            assert torch.equal(vo[a:a + int(kl[l])], vd[l, g, idx])
+        off += Hkv * int(kl[l])
+    return diffs
+
+
+@pytest.mark.parametrize("name", ["tiny", "kv2_32k", "kv2_131k"])
+def test_compress_block_small_workloads(K, name):
+    w = SMALL[name]
+    x = gen.single_inputs(w)
+    keep = w.keep_per_layer()
+    diffs = compress_and_check(K, w.shape, x["q"], x["k"], x["v"], keep * w.shape.layers, what=name)
+    print(f"{name}: {diffs} kept positions inside the tie band differ")
+
+
+def test_compress_block_keep_everything(K):
+    w = SMALL["kv2_32k"]
+    x = gen.single_inputs(w)
+    compress_and_check(K, w.shape, x["q"], x["k"], x["v"], 10 ** 9, what="keep all")
+
+
+def test_episodic_small(K):
+    from kv_cache_compression_kvs_amd import drivers
+    w = SMALL["episodic"]
+    x = gen.episodic_inputs(w)
+    s = w.shape
+    outs = drivers.episodic(x["k"].cuda(), x["v"].cuda(), x["q_episodes"].cuda(), x["sens"],
+                            w.alpha, w.total_budget, s.n_sinks, s.chunk_size, s.q_per_chunk)
+    torch.cuda.synchronize()
+    kl, ref = O.episodic(f64(x["k"]), f64(x["v"]), f64(x["q_episodes"]), x["sens"], w.alpha,
+                         w.total_budget, s.n_sinks, s.chunk_size, s.q_per_chunk)
+    kd = x["k"].cuda()
+    for e, (o, r) in enumerate(zip(outs, ref)):
+        assert o["k_per_layer"].tolist() == kl.tolist()
+        assert_scores_close(f64(o["scores"]).reshape(r["scores"].shape), r["scores"], f"ep {e}")
+        per = drivers.split_packed(o["kept"], kl, s.kv_heads)
+        per_k = drivers.split_packed(o["k"], kl, s.kv_heads)
+        for l in range(s.layers):
+            for g in range(s.kv_heads):
+                assert_kept_match(per[l][g].cpu().numpy(), r["scores"][l, g], int(kl[l]),
+                                  s.n_sinks, f"ep {e} l={l} g={g}")
+                assert torch.equal(per_k[l][g], kd[l, g, per[l][g].long()])
+
+
+def test_block_loop_teacher_forced(K):
+    """Each scoring step starts from the oracle's cache and must reproduce the
+    oracle's scores and kept positions for that step."""
+    from kv_cache_compression_kvs_amd import drivers
+    w = SMALL["epicache_block_loop"]
+    s = w.shape
+    x = gen.block_loop_inputs(w)
+    recs = O.block_loop(f64(x["k_tokens"]), f64(x["v_tokens"]), f64(x["q_steps"]),
+                        w.block_len, w.budget_m, s.n_sinks)
+    loop = drivers.BlockLoop(s.layers, s.q_heads, s.kv_heads, s.head_dim, torch.bfloat16,
+                             w.block_len, w.budget_m, s.n_sinks, s.q_per_chunk)
+    kt, vt, qs = x["k_tokens"].cuda(), x["v_tokens"].cuda(), x["q_steps"].cuda()
+    scored = 0
+    for b, rec in enumerate(recs):
+        nb = min(w.block_len, kt.shape[2] - b * w.block_len)
+        n_prev = rec["n_cache"] - nb
+        loop.cur = 0
+        loop.n = n_prev
+        if n_prev:
+            loop.k[0][:, :, :n_prev] = torch.from_numpy(rec["k"][:, :, :n_prev]).bfloat16().cuda()
+            loop.v[0][:, :, :n_prev] = torch.from_numpy(rec["v"][:, :, :n_prev]).bfloat16().cuda()
+        before_k = torch.from_numpy(rec["k"]).bfloat16().cuda()
+        did = loop.step(b, kt, vt, qs[b])
+        torch.cuda.synchronize()
+        assert did == ("kept" in rec)
+        if not did:
+            continue
+        scored += 1
+        n = rec["n_cache"]
+        g_scores = loop.scores[:s.layers * s.kv_heads * n].view(s.layers, s.kv_heads, n)
+        assert_scores_close(f64(g_scores), rec["scores"], f"block {b}")
+        kk = loop.kept.view(s.layers, s.kv_heads, w.budget_m)
+        ck, _ = loop.cache()
+        for l in range(s.layers):
+            for g in range(s.kv_heads):
+                assert_kept_match(kk[l, g].cpu().numpy(), rec["scores"][l, g], w.budget_m,
+                                  s.n_sinks, f"block {b} l={l} g={g}")
+                assert torch.equal(ck[l, g], before_k[l, g, kk[l, g].long()])
+    assert scored == sum("kept" in r for r in recs) and scored >= 3
+
+
+def test_block_loop_free_running_positions(K):
+    from kv_cache_compression_kvs_amd import drivers
+    w = SMALL["epicache_block_loop"]
+    s = w.shape
+    x = gen.block_loop_inputs(w)
+    recs = O.block_loop(f64(x["k_tokens"]), f64(x["v_tokens"]), f64(x["q_steps"]),
+                        w.block_len, w.budget_m, s.n_sinks)
+    loop = drivers.BlockLoop(s.layers, s.q_heads, s.kv_heads, s.head_dim, torch.bfloat16,
+                             w.block_len, w.budget_m, s.n_sinks, s.q_per_chunk)
+    pos = {"p": torch.zeros(s.layers, s.kv_heads, 0, dtype=torch.long)}
+
+    def on_step(b, lp, did):
+        nb = min(w.block_len, x["k_tokens"].shape[2] - b * w.block_len)
+        newp = torch.arange(b * w.block_len, b * w.block_len + nb).expand(s.layers, s.kv_heads, nb)
+        p = torch.cat([pos["p"], newp], dim=2)
+        if did:
+            kk = lp.kept.view(s.layers, s.kv_heads, w.budget_m).long().cpu()
+            p = torch.gather(p, 2, kk)
+        pos["p"] = p
+
+    loop.run(x["k_tokens"].cuda(), x["v_tokens"].cuda(), x["q_steps"].cuda(), on_step=on_step)
+    torch.cuda.synchronize()
+    final = recs[-1]["pos"]
+    if "kept" in recs[-1]:
+        final = np.take_along_axis(final, np.stack(recs[-1]["kept"]), axis=2)
+    got = pos["p"].numpy()
+    mismatch = sum(len(set(got[l, g]) ^ set(final[l, g]))
+                   for l in range(s.layers) for g in range(s.kv_heads))
+    total = s.layers * s.kv_heads * w.budget_m
+    print(f"free-running divergence: {mismatch} of {total}")
+    assert mismatch <= 0.01 * total
+    ck, _ = loop.cache()
+    kt = x["k_tokens"].cuda()
+    for l in range(s.layers):
+        for g in range(s.kv_heads):
+            assert torch.equal(ck[l, g], kt[l, g, torch.from_numpy(got[l, g]).cuda()])

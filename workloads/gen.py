@@ -296,9 +296,14 @@ def episodic_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
                 for e in range(E):
                     gq = _gen(device, seed, w.name, "q", l, h, e)
                     q[e, l, h] = _store(mu[e] + torch.randn(Nq, d, generator=gq, device=device), dt)
+    return {"k": k, "v": v, "q_episodes": q, "sens": sensitivities(w, seed), "topics": topics}
+
+
+def sensitivities(w: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """Per-layer sensitivities s_l ~ U[0.5, 1.5], float64 [L]."""
+    seed = w.seed if seed is None else seed
     rs = np.random.Generator(np.random.Philox(_seed(seed, w.name, "sens")))
-    sens = rs.uniform(0.5, 1.5, size=L)
-    return {"k": k, "v": v, "q_episodes": q, "sens": sens, "topics": topics}
+    return rs.uniform(0.5, 1.5, size=w.shape.layers)
 
 
 # --------------------------------------------------------------------------
