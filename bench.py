@@ -96,8 +96,8 @@ def main():
         if w.kind == "episodic":
             x = gen.episodic_inputs(w, device=dev)
             qs = x["q_episodes"]
-            kl = list(K.kvs_layer_budgets(s.layers, w.total_budget, x["sens"], w.alpha,
-                                          s.n_cache, s.n_sinks))
+            kl = [int(v) for v in K.kvs_layer_budgets(s.layers, w.total_budget, x["sens"], w.alpha,
+                                                      s.n_cache, s.n_sinks)]
             total, sens, alpha = w.total_budget, x["sens"], w.alpha
         else:
             x = gen.single_inputs(w, device=dev)

@@ -48,4 +48,17 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t grid) {
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Generic LDS pointer as the address-space-3 pointer the LDS DMA builtin takes.
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
+  return (__attribute__((address_space(3))) void*)(p);
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 family
+// encoding: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 }  // namespace kvs

@@ -49,11 +49,15 @@ struct P1Args {
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
-  constexpr int KS = D / 16;                          // MFMA steps along d
-  constexpr int PIECES = D / 8;                       // 16-byte pieces per row
-  constexpr int LOADS = kP1Keys * PIECES / kThreads;  // pieces per thread per tile
-  constexpr int LD = D + 8;                           // padded LDS row (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kP1Keys * LD];
+  constexpr int KS = D / 16;                       // MFMA steps along d
+  constexpr int ROWB = D * 2;                      // bytes per key row
+  constexpr int CPR = ROWB / 16;                   // 16-byte chunks per row
+  constexpr int TILEB = kP1Keys * ROWB;            // bytes per key tile
+  constexpr int LPT = TILEB / (kThreads * 16);     // DMA instructions per wave per tile
+  // Four key tiles in flight through a ring of LDS buffers filled by direct
+  // global->LDS loads.  Separate arrays (indexed statically below) let the
+  // compiler see that a DMA into one buffer never aliases reads of another.
+  __shared__ __attribute__((aligned(16))) uint8_t r0[TILEB], r1[TILEB], r2[TILEB], r3[TILEB];
 
   const int64_t tau = xcd_remap(blockIdx.x, gridDim.x);
   if (tau >= a.n_logical) return;
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
 
   const int64_t unit_row0 = (l * a.Hq + g * a.G) * a.Nq;
   const uint16_t* qunit = a.q + unit_row0 * D;
-  const uint16_t* kslab = a.k + (l * a.Hkv + g) * a.kv_stride * D;
+  const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(a.k + (l * a.Hkv + g) * a.kv_stride * D);
   const int64_t row_w = rb * kP1Rows + wave * 64;
 
   bf16x8 qf[2][KS];
@@ -83,76 +87,158 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
 
   const int64_t kbeg = split * a.keys_per_split;
   const int64_t kend = min(kbeg + a.keys_per_split, a.N);
-  const int64_t ntiles = ceil_div(kend - kbeg, kP1Keys);
+  const int64_t nkeys = kend - kbeg;
+  const int64_t nfull = nkeys / kP1Keys;
+  const int64_t ntiles = ceil_div(nkeys, kP1Keys);
+  const int64_t ngroups = nfull / 4;
 
   float m[2] = {-INFINITY, -INFINITY};
   float ls[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   const float c1 = a.c1;
 
-  u32x4 pre[LOADS];
-  auto gload = [&](int64_t tile) {
-    const int64_t base = kbeg + tile * kP1Keys;
+  // Tile layout in LDS: row r (a key), 16-byte chunk c at r*ROWB + ((c ^ (r % CPR)) * 16).
+  // The XOR swizzle makes the fragment reads (32 rows, same chunk) hit
+  // distinct banks.  Wave w's i-th DMA fills LDS chunks [(4i+w)*64, +64),
+  // lane by lane, so each lane fetches the global chunk that lands there.
+  auto dma = [&](uint8_t* buf, int64_t tile) __attribute__((always_inline)) {
+    const int64_t key0 = kbeg + tile * kP1Keys;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + i * kThreads;
-      int64_t key = base + c / PIECES;
-      if (key > a.N - 1) key = a.N - 1;  // clamped rows are masked below
-      pre[i] = *(const u32x4*)(kslab + key * D + (c % PIECES) * 8);
+    for (int i = 0; i < LPT; ++i) {
+      const int q = (i * 4 + wave) * 64 + lane;
+      const int row = q / CPR, slot = q % CPR;
+      int64_t key = key0 + row;
+      if (key > a.N - 1) key = a.N - 1;  // rows past the end are masked or unused
+      __builtin_amdgcn_global_load_lds(kbytes + key * ROWB + (slot ^ (row & (CPR - 1))) * 16,
+                                       lds_ptr(buf + (i * 4 + wave) * 1024), 16, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + i * kThreads;
-      *(u32x4*)(&sk[buf][(c / PIECES) * LD + (c % PIECES) * 8]) = pre[i];
-    }
+  auto afrag = [&](const uint8_t* buf, int kb, int ks) __attribute__((always_inline)) -> bf16x8 {
+    const int row = kb * 32 + col;
+    const int c = 2 * ks + half;
+    return *(const bf16x8*)(buf + row * ROWB + ((c ^ (row & (CPR - 1))) * 16));
   };
-  auto update = [&](int qb, f32x16 z) {
+
+  // The update of one query block split in two parts: the head finds the
+  // block max, moves the running max and rescales the partial sums; the
+  // element part adds 2^(z c1 - max) for elements [e0, e1).
+  auto update_head = [&](const f32x16& z, float& mref, float (&l4)[4]) -> float {
     float mx = max3f(max3f(z[0], z[1], z[2]), max3f(z[3], z[4], z[5]), max3f(z[6], z[7], z[8]));
     mx = max3f(mx, max3f(z[9], z[10], z[11]), max3f(z[12], z[13], z[14]));
     mx = fmaxf(mx, z[15]);
-    const float mn = fmaxf(m[qb], mx * c1);
-    const float ms = (mn == -INFINITY) ? 0.f : mn;
-    const float sc = exp2_hw(m[qb] - ms);
+    const float mn = fmaxf(mref, mx * c1);
+    const float msh = (mn == -INFINITY) ? 0.f : mn;
+    const float sc = exp2_hw(mref - msh);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ls[qb][j] *= sc;
+    for (int j = 0; j < 4; ++j) l4[j] *= sc;
+    mref = mn;
+    return msh;
+  };
+  auto update_elems = [&](const f32x16& z, float (&l4)[4], float msh, int e0, int e1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ls[qb][i & 3] += exp2_hw(fmaf(z[i], c1, -ms));
-    m[qb] = mn;
+    for (int e = 0; e < 16; ++e)
+      if (e >= e0 && e < e1) l4[e & 3] += exp2_hw(fmaf(z[e], c1, -msh));
+  };
+  auto update = [&](int qb, const f32x16& z) __attribute__((always_inline)) {
+    const float msh = update_head(z, m[qb], ls[qb]);
+    update_elems(z, ls[qb], msh, 0, 16);
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int64_t t = 0; t < ntiles; ++t) {
-    const int buf = (int)(t & 1);
-    if (t + 1 < ntiles) gload(t + 1);
-    const int64_t valid = kend - (kbeg + t * kP1Keys);
+  // Software pipeline over 32-key blocks: the MFMAs of block j and the
+  // softmax update of block j-1 sit in one basic block; after each MFMA one
+  // slice of the update follows and a scheduling fence keeps that order, so
+  // the vector ALU works while the MFMA occupies the matrix pipe.
+  f32x16 p0, p1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    p0[i] = -INFINITY;
+    p1[i] = -INFINITY;
+  }
+  auto compute_tile = [&](const uint8_t* buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc0 = {}, acc1 = {};
-      const uint16_t* arow = &sk[buf][(kb * 32 + col) * LD + half * 8];
+      bf16x8 af[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 av = *(const bf16x8*)(arow + ks * 16);
-        acc0 = mfma32x32x16(av, qf[0][ks], acc0);
-        acc1 = mfma32x32x16(av, qf[1][ks], acc1);
+      for (int ks = 0; ks < KS; ++ks) af[ks] = afrag(buf, kb, ks);
+      f32x16 n0 = {}, n1 = {};
+      constexpr int NS = 2 * KS;      // MFMAs (and update slices) per block
+      constexpr int HALF = NS / 2;    // slices per query block
+      float ms0 = 0.f, ms1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        if ((i & 1) == 0) n0 = mfma32x32x16(af[i >> 1], qf[0][i >> 1], n0);
+        else n1 = mfma32x32x16(af[i >> 1], qf[1][i >> 1], n1);
+        if (i == 0) ms0 = update_head(p0, m[0], ls[0]);
+        else if (i < HALF) update_elems(p0, ls[0], ms0, 16 * (i - 1) / (HALF - 1), 16 * i / (HALF - 1));
+        else if (i == HALF) ms1 = update_head(p1, m[1], ls[1]);
+        else update_elems(p1, ls[1], ms1, 16 * (i - HALF - 1) / (HALF - 1), 16 * (i - HALF) / (HALF - 1));
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (valid < kP1Keys) {
+      p0 = n0;
+      p1 = n1;
+    }
+  };
+  // Tile u lives in buffer u % 4.  Before computing it: wait until at most
+  // the two younger tiles' DMAs are outstanding, meet at the barrier (every
+  // wave's share of tile u has landed and every wave is done with tile u-1),
+  // then start the DMA of tile u + 3 into tile u-1's buffer.
+  auto step = [&](const uint8_t* cur, uint8_t* nxt, int64_t u) __attribute__((always_inline)) {
+    wait_vmcnt<2 * LPT>();
+    __builtin_amdgcn_s_barrier();
+    dma(nxt, u + 3);
+    compute_tile(cur);
+  };
+
+  dma(r0, 0);
+  dma(r1, 1);
+  dma(r2, 2);
+  for (int64_t gi = 0; gi < ngroups; ++gi) {
+    const int64_t u = gi * 4;
+    step(r0, r3, u);
+    step(r1, r0, u + 1);
+    step(r2, r1, u + 2);
+    step(r3, r2, u + 3);
+  }
+  update(0, p0);
+  update(1, p1);
+
+  // Remaining tiles (fewer than four full tiles and a ragged tail), one at a
+  // time with masking.  Tiles below `issued` already have their DMA in flight.
+  int64_t issued = ngroups * 4 + 3;
+  for (int64_t u = ngroups * 4; u < ntiles; ++u) {
+    uint8_t* buf = (u & 3) == 0 ? r0 : (u & 3) == 1 ? r1 : (u & 3) == 2 ? r2 : r3;
+    if (u >= issued) {
+      __builtin_amdgcn_s_barrier();  // every wave is done with the buffer's previous tile
+      dma(buf, u);
+      ++issued;
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    const int64_t valid = nkeys - u * kP1Keys;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (kb * 32 + acc_row(i, lane) >= valid) {
-            acc0[i] = -INFINITY;
-            acc1[i] = -INFINITY;
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb * 32 < valid) {
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 av = afrag(buf, kb, ks);
+          acc0 = mfma32x32x16(av, qf[0][ks], acc0);
+          acc1 = mfma32x32x16(av, qf[1][ks], acc1);
+        }
+        if (valid < kP1Keys) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if (kb * 32 + acc_row(i, lane) >= valid) {
+              acc0[i] = -INFINITY;
+              acc1[i] = -INFINITY;
+            }
           }
         }
+        update(0, acc0);
+        update(1, acc1);
       }
-      update(0, acc0);
-      update(1, acc1);
     }
-    if (t + 1 < ntiles) sstore(buf ^ 1);
-    __syncthreads();
   }
+  wait_vmcnt<0>();  // no DMA may still target LDS when the workgroup exits
 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -250,8 +336,8 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_bf16(P2Args a) {
 
   u32x4 pre[LOADS];
   float cpre = INFINITY;
-  auto urow_of = [&](int64_t rho) { return (rho / a.nq) * a.Nq + r * a.nq + (rho % a.nq); };
-  auto gload = [&](int64_t tl) {
+  auto urow_of = [&](int64_t rho) __attribute__((always_inline)) { return (rho / a.nq) * a.Nq + r * a.nq + (rho % a.nq); };
+  auto gload = [&](int64_t tl) __attribute__((always_inline)) {
     const int64_t base = tl * ROWS;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -268,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_bf16(P2Args a) {
       cpre = (rho < nrows) ? a.c2[unit_row0 + urow_of(rho)] : INFINITY;
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int c = tid + i * kThreads;
