@@ -35,6 +35,8 @@ int check(const kvs_problem* p) {
   if (p->kv_row_stride != 0 && p->kv_row_stride < p->n_cache) return KVS_E_SHAPE;
   if (p->dtype != KVS_F32 && p->dtype != KVS_BF16) return KVS_E_DTYPE;
   if (p->flags != 0) return KVS_E_SHAPE;
+  // the scoring kernels index a chunk's rows (G * nq of them) in 32 bits
+  if ((int64_t)(p->q_heads / p->kv_heads) * p->q_per_chunk >= (int64_t(1) << 31)) return KVS_E_SHAPE;
   const int64_t R = chunks_of(*p);
   const int64_t nq_total = R * p->q_per_chunk;
   if (R > 0 && nq_total / R != p->q_per_chunk) return KVS_E_SHAPE;

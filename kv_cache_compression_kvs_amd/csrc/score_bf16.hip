@@ -282,6 +282,7 @@ struct P2Args {
   float* scores;
   int64_t Nq, N, S, m, nq, kv_stride, R, tiles, n_logical;
   int32_t Hq, Hkv, G;
+  uint32_t nq_mul, nq_shift;  // rho / nq as (umulhi(rho, nq_mul) + rho) >> nq_shift
   float c1, inv_c1;
 };
 
@@ -336,7 +337,13 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_bf16(P2Args a) {
 
   u32x4 pre[LOADS];
   float cpre = INFINITY;
-  auto urow_of = [&](int64_t rho) __attribute__((always_inline)) { return (rho / a.nq) * a.Nq + r * a.nq + (rho % a.nq); };
+  // unit row of chunk-row rho: head rho / nq of the group, query rho % nq of chunk r
+  const uint32_t nq32 = (uint32_t)a.nq;
+  auto urow_of = [&](int64_t rho) __attribute__((always_inline)) -> int64_t {
+    const uint32_t x = (uint32_t)rho;
+    const uint32_t t = (__umulhi(x, a.nq_mul) + x) >> a.nq_shift;
+    return (int64_t)t * a.Nq + r * a.nq + (x - t * nq32);
+  };
   auto gload = [&](int64_t tl) __attribute__((always_inline)) {
     const int64_t base = tl * ROWS;
 #pragma unroll
@@ -403,6 +410,15 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_bf16(P2Args a) {
   }
 }
 
+// Exact unsigned division by a runtime divisor through a multiply-high:
+// n / d == (umulhi(n, mul) + n) >> shift for every n < 2^31.
+inline void fast_div(uint32_t d, uint32_t* mul, uint32_t* shift) {
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  *shift = s;
+  *mul = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1);
+}
+
 inline int64_t pad8(int64_t n) { return (n + 7) & ~int64_t(7); }
 
 template <int D>
@@ -467,6 +483,7 @@ int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
   a2.G = a1.G;
   a2.c1 = c1;
   a2.inv_c1 = inv_c1;
+  fast_div((uint32_t)p.q_per_chunk, &a2.nq_mul, &a2.nq_shift);
   {
     TraceScope ts("score_pass2_bf16", st);
     hipLaunchKernelGGL(pass2_bf16<D>, dim3((unsigned)pad8(a2.n_logical)), dim3(kThreads), 0, st, a2);
