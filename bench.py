@@ -169,9 +169,10 @@ def main():
         # in the block loop and the single-shot workloads)
         per_launch = p1_flops[0]
         achieved = per_launch / (avg(p1_name) * 1e-3) / 1e12
-        roofline = {"kernel": p1_name, "bound": "mfma", "achieved": round(achieved, 2),
+        roofline = {"kernel": p1_name, "bound": "mfma" if s.dtype == "bf16" else "alu",
+                    "achieved": round(achieved, 2),
                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                    "traffic": None, "flops_per_launch": per_launch,
+                    "traffic": profiled_traffic(w.name, p1_name), "flops_per_launch": per_launch,
                     "avg_launch_ms": round(avg(p1_name), 5)}
     score_ms = tot(p1_name) + tot("score_merge_splits") + tot(p2_name)
     sc_ms = tot("select") + tot("compact")
@@ -210,46 +211,75 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
+def profiled_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy), or
+    None if there is none or the kernel source changed since it was taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        m = re.match(r"kernel=(\S+) traffic_bytes_per_launch=(\d+) source=(\S+) sha256_16=([0-9a-f]+)",
+                     line.strip())
+        if m and m.group(1) == kernel:
+            src = os.path.join(ROOT, m.group(3))
+            if not os.path.exists(src):
+                return None
+            h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+            return int(m.group(2)) if h == m.group(4) else None
+    return None
+
+
 def cpu_baseline(w, x, budget_s, kl):
-    """The oracle, as it is, on whole (layer, KV head) units of one scoring call,
-    until about budget_s seconds have been spent; reported in the metric's unit."""
+    """The oracle, as it is, on whole (layer, KV head) units of the workload
+    until about budget_s seconds have been spent; reported in the metric's
+    unit.  For the block loop a unit is carried through the oracle's own block
+    loop (all of its scoring steps); otherwise one unit is scored and selected."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import oracle as O
 
     s = w.shape
-    if w.kind == "block_loop":
-        n = w.budget_m + w.block_len             # the first scoring call sees tokens [0, n)
-        k_all = x["k_tokens"][:, :, :n]
-        q_all = x["q_steps"][2]
-        chunk = n - s.n_sinks
-    else:
-        n = s.n_cache
-        k_all = x["k"]
-        q_all = x["q_episodes"][0] if w.kind == "episodic" else x["q"]
-        chunk = s.chunk_size
     G = s.group
+
+    def f64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
     done_tokens, spent, units = 0, 0.0, 0
     for l in range(s.layers):
         for g in range(s.kv_heads):
-            qg = q_all[l, g * G:(g + 1) * G].float().cpu().numpy().astype(np.float64)
-            kg = k_all[l, g].float().cpu().numpy().astype(np.float64)
-            t = time.perf_counter()
-            sc = O.unit_scores(qg, kg, s.n_sinks, chunk, s.q_per_chunk)
-            O.select_unit(sc, int(kl[l]), s.n_sinks)
-            spent += time.perf_counter() - t
-            done_tokens += n
+            if w.kind == "block_loop":
+                kt = f64(x["k_tokens"][l:l + 1, g:g + 1])
+                vt = f64(x["v_tokens"][l:l + 1, g:g + 1])
+                qs = f64(x["q_steps"][:, l:l + 1, g * G:(g + 1) * G])
+                t = time.perf_counter()
+                recs = O.block_loop(kt, vt, qs, w.block_len, w.budget_m, s.n_sinks)
+                spent += time.perf_counter() - t
+                done_tokens += sum(r["n_cache"] for r in recs if "kept" in r)
+            else:
+                q_all = x["q_episodes"][0] if w.kind == "episodic" else x["q"]
+                qg = f64(q_all[l, g * G:(g + 1) * G])
+                kg = f64(x["k"][l, g])
+                t = time.perf_counter()
+                sc = O.unit_scores(qg, kg, s.n_sinks, s.chunk_size, s.q_per_chunk)
+                O.select_unit(sc, int(kl[l]), s.n_sinks)
+                spent += time.perf_counter() - t
+                done_tokens += s.n_cache
             units += 1
             if spent >= budget_s:
                 break
         if spent >= budget_s:
             break
     threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    what = ("the oracle's block loop (every scoring step, selection and compaction)"
+            if w.kind == "block_loop" else "float64 scores and selection of one scoring call")
     return {"value": done_tokens / spent, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{units} (layer, KV head) units of one {n}-position scoring call of "
-                      f"{w.name}: float64 scores and selection, {spent:.1f} s",
+            "sample": f"{units} of {s.layers * s.kv_heads} (layer, KV head) units of {w.name}: "
+                      f"{what}, {spent:.1f} s",
             "host_cpus": os.cpu_count()}
 
 

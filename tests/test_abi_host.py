@@ -47,6 +47,15 @@ def test_every_declared_symbol_is_exported(K):
         assert getattr(h, n) is not None
 
 
+def test_library_has_no_unresolved_own_symbols(K):
+    # a kernel whose launch stub the host compiler failed to emit shows up as an
+    # undefined kvs:: symbol that would only fail when the library is loaded
+    out = subprocess.run(["nm", "-D", "--undefined-only", "-C", K.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    own = [l for l in out.splitlines() if "kvs::" in l]
+    assert not own, own
+
+
 def test_status_strings_and_version(K):
     assert K.kvs_status_string(0) == "ok"
     for s in range(1, 8):
