@@ -76,6 +76,11 @@ typedef enum kvs_dtype {
  *   K, V    [L, Hkv, kv_row_stride, d] of dtype; rows [0, N) of every
  *           (layer, KV head) slab are read.  kv_row_stride = 0 means N.
  *   scores  [L, Hkv, N] fp32
+ *
+ * Size limits (KVS_E_SHAPE otherwise): N <= 2^31 - 1; one (layer, KV head)
+ * slab of keys, N * d * 4 bytes, and one KV head's query rows,
+ * G * Nq * d * 4 bytes, each below 4 GiB (the kernels address them with
+ * 32-bit offsets); every launch grid below 2^31 workgroups.
  */
 typedef struct kvs_problem {
   int32_t layers;

@@ -9,7 +9,8 @@
 // each lane moves one 16-byte piece, a 256-thread workgroup moves
 // 256 / pieces_per_row rows per pass and four passes per launch slot, with all
 // loads issued before the stores so that eight 16-byte reads per lane
-// (K and V) are in flight.
+// (K and V) are in flight.  Loads and stores carry the nontemporal hint: the
+// streams are far larger than the caches and are not re-read by this kernel.
 #include "kvs_device.h"
 #include "kvs_internal.h"
 #include "kvs_trace.h"
@@ -49,29 +50,27 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   const int piece = threadIdx.x % LPR;
   const int rsub = threadIdx.x / LPR;
 
+  // Every load is unconditional (from a clamped, in-bounds row) so that all of
+  // them are in flight at once; only the stores are guarded.
+  int64_t idx[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) idx[u] = kp[min(t0 + u * RPP + rsub, kl - 1)];
   u32x4 kb[kUnroll], vb[kUnroll];
   bool ok[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const int64_t t = t0 + u * RPP + rsub;
-    ok[u] = false;
-    if (t < kl) {
-      const int64_t idx = kp[t];
-      ok[u] = idx >= 0 && idx < a.n_cache;  // rows outside the cache are skipped
-      if (ok[u]) {
-        const int64_t src = idx * a.row_bytes + piece * 16;
-        kb[u] = *(const u32x4*)(ks + src);
-        vb[u] = *(const u32x4*)(vs + src);
-      }
-    }
+    ok[u] = t0 + u * RPP + rsub < kl && idx[u] >= 0 && idx[u] < a.n_cache;  // rows outside the cache are skipped
+    const int64_t src = (ok[u] ? idx[u] : 0) * a.row_bytes + piece * 16;
+    kb[u] = __builtin_nontemporal_load((const u32x4*)(ks + src));
+    vb[u] = __builtin_nontemporal_load((const u32x4*)(vs + src));
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t t = t0 + u * RPP + rsub;
     if (ok[u]) {
       const int64_t dst = t * a.row_bytes + piece * 16;
-      *(u32x4*)(ko + dst) = kb[u];
-      *(u32x4*)(vo + dst) = vb[u];
+      __builtin_nontemporal_store(kb[u], (u32x4*)(ko + dst));
+      __builtin_nontemporal_store(vb[u], (u32x4*)(vo + dst));
     }
   }
 }
@@ -91,13 +90,13 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const uint8_t* src, in
   u32x4 b[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const int64_t t = t0 + u * RPP + rsub;
-    if (t < n_rows) b[u] = *(const u32x4*)(s + t * row_bytes + piece * 16);
+    const int64_t t = min(t0 + u * RPP + rsub, n_rows - 1);  // unconditional, in bounds
+    b[u] = __builtin_nontemporal_load((const u32x4*)(s + t * row_bytes + piece * 16));
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t t = t0 + u * RPP + rsub;
-    if (t < n_rows) *(u32x4*)(d + t * row_bytes + piece * 16) = b[u];
+    if (t < n_rows) __builtin_nontemporal_store(b[u], (u32x4*)(d + t * row_bytes + piece * 16));
   }
 }
 

@@ -33,6 +33,8 @@ int check(const kvs_problem* p) {
   if (p->n_cache < 0 || p->n_cache > INT32_MAX) return KVS_E_SHAPE;
   if (p->n_sinks < 0 || p->chunk_size < 1 || p->q_per_chunk < 1) return KVS_E_SHAPE;
   if (p->kv_row_stride != 0 && p->kv_row_stride < p->n_cache) return KVS_E_SHAPE;
+  // one (layer, KV head) slab of keys is addressed with 32-bit byte offsets
+  if (p->n_cache * p->head_dim * 4 >= (int64_t(1) << 32)) return KVS_E_SHAPE;
   if (p->dtype != KVS_F32 && p->dtype != KVS_BF16) return KVS_E_DTYPE;
   if (p->flags != 0) return KVS_E_SHAPE;
   // the scoring kernels index a chunk's rows (G * nq of them) in 32 bits
@@ -40,6 +42,11 @@ int check(const kvs_problem* p) {
   const int64_t R = chunks_of(*p);
   const int64_t nq_total = R * p->q_per_chunk;
   if (R > 0 && nq_total / R != p->q_per_chunk) return KVS_E_SHAPE;
+  // one KV head's query rows (G * R * nq of them) are addressed with 32-bit
+  // byte offsets as well
+  if (nq_total > INT32_MAX ||
+      (int64_t)(p->q_heads / p->kv_heads) * nq_total * p->head_dim * 4 >= (int64_t(1) << 32))
+    return KVS_E_SHAPE;
   const ScorePlan pl = plan_score(*p);
   // every launch grid must fit the 31-bit x dimension
   if (p->dtype == KVS_BF16 && pl.units * pl.splits * pl.row_blocks + 8 > kMaxGrid)

@@ -48,6 +48,10 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t grid) {
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Third dword of a raw (offset-mode) buffer resource on gfx9-family parts:
+// 32-bit data format, no swizzle.  Loads at or past num_records return zero.
+constexpr int kBufferFlags = 0x00020000;
+
 // Generic LDS pointer as the address-space-3 pointer the LDS DMA builtin takes.
 __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(void* p) {
   return (__attribute__((address_space(3))) void*)(p);

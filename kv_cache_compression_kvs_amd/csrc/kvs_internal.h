@@ -52,8 +52,11 @@ int launch_append(int32_t slabs, int64_t row_bytes, const void* src, int64_t src
 
 // Pass-1 tiling constants shared by the planner and the kernels.
 constexpr int kP1Rows = 256;      // query rows per pass-1 workgroup (4 waves x 64)
-constexpr int kP1Keys = 64;       // keys per pass-1 LDS tile
-constexpr int kP2Keys = 256;      // keys per pass-2 workgroup (4 waves x 64)
+constexpr int kP1Keys = 128;      // keys per pass-1 LDS tile
+constexpr int kP1Ring = 2;        // pass-1 LDS tiles in flight
+constexpr int kP2Waves = 4;       // pass-2 waves per workgroup, 64 keys each
+constexpr int kP2Keys = kP2Waves * 64;  // keys per pass-2 workgroup
+constexpr int kP2Ring = 2;        // pass-2 LDS query tiles in flight
 constexpr int kMaxSplits = 64;
 
 }  // namespace kvs

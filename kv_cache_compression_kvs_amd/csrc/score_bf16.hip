@@ -19,11 +19,10 @@
 //           per position at the end (max of exp = exp of max).
 //
 // Pass 1 workgroup: 4 waves x 64 query rows (two 32-column MFMA blocks per
-// wave, Q fragments resident in VGPRs); keys stream through a double-buffered
-// LDS tile of 64 rows padded by 16 bytes per row (conflict-free 16-byte reads).
-// Pass 2 workgroup: 4 waves x 64 keys resident in VGPRs; the chunk's query
-// rows (all heads of the group) stream through LDS in tiles of 64 rows
-// together with their c2 values.
+// wave, Q fragments resident in VGPRs); keys stream through a ring of LDS
+// tiles filled by direct global->LDS loads.  Pass 2 workgroup: 64 keys per
+// wave resident in VGPRs; the chunk's query rows (all heads of the group)
+// stream through a ring of LDS tiles together with their -c2/c1 values.
 #include <math.h>
 
 #include "kvs_device.h"
@@ -38,26 +37,32 @@ constexpr int kThreads = 256;
 struct P1Args {
   const uint16_t* q;
   const uint16_t* k;
-  float* c2;        // [total_rows], written when splits == 1
+  float* c2n;       // [total_rows] -c2 / c1, written when splits == 1
   float* part_m;    // [splits][total_rows]
   float* part_l;    // [splits][total_rows]
   int64_t Nq, N, kv_stride, rows_per_unit, row_blocks, splits, keys_per_split, total_rows;
   int64_t n_logical;
   int32_t Hq, Hkv, G;
-  float c1;
+  float c1, inv_c1;
 };
 
-template <int D>
+template <int D, int TK, int NBUF>
 __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
   constexpr int KS = D / 16;                       // MFMA steps along d
   constexpr int ROWB = D * 2;                      // bytes per key row
   constexpr int CPR = ROWB / 16;                   // 16-byte chunks per row
-  constexpr int TILEB = kP1Keys * ROWB;            // bytes per key tile
+  constexpr int NB = TK / 32;                      // 32-key blocks per tile
+  constexpr int TILEB = TK * ROWB;                 // bytes per key tile
   constexpr int LPT = TILEB / (kThreads * 16);     // DMA instructions per wave per tile
-  // Four key tiles in flight through a ring of LDS buffers filled by direct
+  static_assert(NBUF >= 2 && NBUF <= 4 && TK % 32 == 0, "ring shape");
+  // NBUF key tiles in flight through a ring of LDS buffers filled by direct
   // global->LDS loads.  Separate arrays (indexed statically below) let the
   // compiler see that a DMA into one buffer never aliases reads of another.
-  __shared__ __attribute__((aligned(16))) uint8_t r0[TILEB], r1[TILEB], r2[TILEB], r3[TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t r0[TILEB], r1[TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t r2[NBUF > 2 ? TILEB : 16], r3[NBUF > 3 ? TILEB : 16];
+  auto ring = [&](int i) __attribute__((always_inline)) -> uint8_t* {
+    return i == 0 ? r0 : i == 1 ? r1 : i == 2 ? r2 : r3;
+  };
 
   const int64_t tau = xcd_remap(blockIdx.x, gridDim.x);
   if (tau >= a.n_logical) return;
@@ -88,9 +93,9 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
   const int64_t kbeg = split * a.keys_per_split;
   const int64_t kend = min(kbeg + a.keys_per_split, a.N);
   const int64_t nkeys = kend - kbeg;
-  const int64_t nfull = nkeys / kP1Keys;
-  const int64_t ntiles = ceil_div(nkeys, kP1Keys);
-  const int64_t ngroups = nfull / 4;
+  const int64_t nfull = nkeys / TK;
+  const int64_t ntiles = ceil_div(nkeys, TK);
+  const int64_t ngroups = nfull / NBUF;
 
   float m[2] = {-INFINITY, -INFINITY};
   float ls[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -100,17 +105,21 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
   // The XOR swizzle makes the fragment reads (32 rows, same chunk) hit
   // distinct banks.  Wave w's i-th DMA fills LDS chunks [(4i+w)*64, +64),
   // lane by lane, so each lane fetches the global chunk that lands there.
+  // That chunk's byte offset inside the tile is the same for every i up to
+  // i * 4096 (r % CPR does not depend on i), so one offset register per lane
+  // serves every DMA and the tile position rides in the scalar offset.  The
+  // buffer resource covers rows [0, N) of this slab: rows past the end read
+  // as zero instead of leaving the slab.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(kbytes), (short)0, (int)(uint32_t)(a.N * ROWB), kBufferFlags);
+  const int lrow = (wave * 64 + lane) / CPR;
+  const uint32_t voff = (uint32_t)(lrow * ROWB + (((wave * 64 + lane) % CPR) ^ (lrow & (CPR - 1))) * 16);
   auto dma = [&](uint8_t* buf, int64_t tile) __attribute__((always_inline)) {
-    const int64_t key0 = kbeg + tile * kP1Keys;
+    const uint32_t base = (uint32_t)((kbeg + tile * TK) * ROWB);
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int q = (i * 4 + wave) * 64 + lane;
-      const int row = q / CPR, slot = q % CPR;
-      int64_t key = key0 + row;
-      if (key > a.N - 1) key = a.N - 1;  // rows past the end are masked or unused
-      __builtin_amdgcn_global_load_lds(kbytes + key * ROWB + (slot ^ (row & (CPR - 1))) * 16,
-                                       lds_ptr(buf + (i * 4 + wave) * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < LPT; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lds_ptr(buf + (i * 4 + wave) * 1024), 16, (int)voff,
+                                               (int)(base + i * 4096), 0, 0);
   };
   auto afrag = [&](const uint8_t* buf, int kb, int ks) __attribute__((always_inline)) -> bf16x8 {
     const int row = kb * 32 + col;
@@ -154,19 +163,26 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
     p1[i] = -INFINITY;
   }
   auto compute_tile = [&](const uint8_t* buf) __attribute__((always_inline)) {
+    constexpr int NS = 2 * KS;      // MFMAs (and update slices) per block
+    constexpr int HALF = NS / 2;    // slices per query block
+    bf16x8 af[2][KS];               // fragments of the current and the next key block
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 af[KS];
+    for (int ks = 0; ks < KS; ++ks) af[0][ks] = afrag(buf, 0, ks);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) af[ks] = afrag(buf, kb, ks);
+    for (int kb = 0; kb < NB; ++kb) {
+      const int cur = kb & 1;
       f32x16 n0 = {}, n1 = {};
-      constexpr int NS = 2 * KS;      // MFMAs (and update slices) per block
-      constexpr int HALF = NS / 2;    // slices per query block
       float ms0 = 0.f, ms1 = 0.f;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        if ((i & 1) == 0) n0 = mfma32x32x16(af[i >> 1], qf[0][i >> 1], n0);
-        else n1 = mfma32x32x16(af[i >> 1], qf[1][i >> 1], n1);
+        if ((i & 1) == 0) {
+          n0 = mfma32x32x16(af[cur][i >> 1], qf[0][i >> 1], n0);
+        } else {
+          n1 = mfma32x32x16(af[cur][i >> 1], qf[1][i >> 1], n1);
+          // fragment ks of this block is dead after its second MFMA: fetch the
+          // next block's fragment ks now, so that block starts without an LDS wait
+          if (kb + 1 < NB) af[cur ^ 1][i >> 1] = afrag(buf, kb + 1, i >> 1);
+        }
         if (i == 0) ms0 = update_head(p0, m[0], ls[0]);
         else if (i < HALF) update_elems(p0, ls[0], ms0, 16 * (i - 1) / (HALF - 1), 16 * i / (HALF - 1));
         else if (i == HALF) ms1 = update_head(p1, m[1], ls[1]);
@@ -177,35 +193,31 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
       p1 = n1;
     }
   };
-  // Tile u lives in buffer u % 4.  Before computing it: wait until at most
-  // the two younger tiles' DMAs are outstanding, meet at the barrier (every
+  // Tile u lives in buffer u % NBUF.  Before computing it: wait until at
+  // most the younger tiles' DMAs are outstanding, meet at the barrier (every
   // wave's share of tile u has landed and every wave is done with tile u-1),
-  // then start the DMA of tile u + 3 into tile u-1's buffer.
-  auto step = [&](const uint8_t* cur, uint8_t* nxt, int64_t u) __attribute__((always_inline)) {
-    wait_vmcnt<2 * LPT>();
+  // then start the DMA of tile u + NBUF - 1 into tile u-1's buffer.
+  auto step = [&](int b, int64_t u) __attribute__((always_inline)) {
+    wait_vmcnt<(NBUF - 2) * LPT>();
     __builtin_amdgcn_s_barrier();
-    dma(nxt, u + 3);
-    compute_tile(cur);
+    dma(ring((b + NBUF - 1) % NBUF), u + NBUF - 1);
+    compute_tile(ring(b));
   };
 
-  dma(r0, 0);
-  dma(r1, 1);
-  dma(r2, 2);
+#pragma unroll
+  for (int b = 0; b + 1 < NBUF; ++b) dma(ring(b), b);
   for (int64_t gi = 0; gi < ngroups; ++gi) {
-    const int64_t u = gi * 4;
-    step(r0, r3, u);
-    step(r1, r0, u + 1);
-    step(r2, r1, u + 2);
-    step(r3, r2, u + 3);
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) step(b, gi * NBUF + b);
   }
   update(0, p0);
   update(1, p1);
 
-  // Remaining tiles (fewer than four full tiles and a ragged tail), one at a
+  // Remaining tiles (fewer than NBUF full tiles and a ragged tail), one at a
   // time with masking.  Tiles below `issued` already have their DMA in flight.
-  int64_t issued = ngroups * 4 + 3;
-  for (int64_t u = ngroups * 4; u < ntiles; ++u) {
-    uint8_t* buf = (u & 3) == 0 ? r0 : (u & 3) == 1 ? r1 : (u & 3) == 2 ? r2 : r3;
+  int64_t issued = ngroups * NBUF + NBUF - 1;
+  for (int64_t u = ngroups * NBUF; u < ntiles; ++u) {
+    uint8_t* buf = ring((int)(u % NBUF));
     if (u >= issued) {
       __builtin_amdgcn_s_barrier();  // every wave is done with the buffer's previous tile
       dma(buf, u);
@@ -213,9 +225,9 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
     }
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    const int64_t valid = nkeys - u * kP1Keys;
+    const int64_t valid = nkeys - u * TK;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NB; ++kb) {
       if (kb * 32 < valid) {
         f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
@@ -224,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
           acc0 = mfma32x32x16(av, qf[0][ks], acc0);
           acc1 = mfma32x32x16(av, qf[1][ks], acc1);
         }
-        if (valid < kP1Keys) {
+        if (valid < TK) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             if (kb * 32 + acc_row(i, lane) >= valid) {
@@ -252,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
     if (half == 0 && r < a.rows_per_unit) {
       const int64_t grow = unit_row0 + r;
       if (a.splits == 1) {
-        a.c2[grow] = M + log2f(L);
+        a.c2n[grow] = -(M + log2f(L)) * a.inv_c1;
       } else {
         a.part_m[split * a.total_rows + grow] = M;
         a.part_l[split * a.total_rows + grow] = L;
@@ -261,10 +273,11 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
   }
 }
 
-// Fixed-order log-sum-exp merge of the per-split partials of pass 1.
+// Fixed-order log-sum-exp merge of the per-split partials of pass 1; writes
+// -c2 / c1 per row, the accumulator start value pass 2 takes.
 __global__ __launch_bounds__(kThreads) void merge_splits(const float* pm, const float* pl,
-                                                        float* c2, int64_t total_rows,
-                                                        int64_t splits) {
+                                                        float* c2n, int64_t total_rows,
+                                                        int64_t splits, float inv_c1) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= total_rows) return;
   float M = -INFINITY;
@@ -272,29 +285,48 @@ __global__ __launch_bounds__(kThreads) void merge_splits(const float* pm, const 
   const float Ms = (M == -INFINITY) ? 0.f : M;
   float L = 0.f;
   for (int64_t s = 0; s < splits; ++s) L += pl[s * total_rows + i] * exp2_hw(pm[s * total_rows + i] - Ms);
-  c2[i] = M + log2f(L);
+  c2n[i] = -(M + log2f(L)) * inv_c1;
 }
 
 struct P2Args {
   const uint16_t* q;
   const uint16_t* k;
-  const float* c2;
+  const float* c2n;     // [total_rows] -c2 / c1 per query row
   float* scores;
   int64_t Nq, N, S, m, nq, kv_stride, R, tiles, n_logical;
   int32_t Hq, Hkv, G;
   uint32_t nq_mul, nq_shift;  // rho / nq as (umulhi(rho, nq_mul) + rho) >> nq_shift
-  float c1, inv_c1;
+  float c1;
 };
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void pass2_bf16(P2Args a) {
+// Pass-2 workgroup: W waves x 64 keys, the keys' fragments resident in VGPRs.
+// The chunk's query rows (all heads of the group, gathered) stream through a
+// ring of NBUF LDS tiles of 64 rows filled by direct global->LDS loads, each
+// tile with its rows' -c2/c1 (one private copy per wave).  A tile is two
+// stages of 32 rows; a stage is 16 MFMAs whose accumulators start at the
+// rows' -c2/c1, and the running max over the previous stage's accumulators
+// is interleaved with them.  Rows past the chunk's last one repeat it, which
+// leaves every max unchanged, so the row loop needs no masking or tail.
+template <int D, int W, int NBUF>
+__global__ __launch_bounds__(W * 64, 8 / W) void pass2_bf16(P2Args a) {
   constexpr int KS = D / 16;
-  constexpr int PIECES = D / 8;
-  constexpr int ROWS = 64;
-  constexpr int LOADS = ROWS * PIECES / kThreads;
-  constexpr int LD = D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sq[2][ROWS * LD];
-  __shared__ float sc[2][ROWS];
+  constexpr int ROWB = D * 2;                 // bytes per query row
+  constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  constexpr int ROWS = 64;                    // query rows per tile
+  constexpr int TILEB = ROWS * ROWB;
+  constexpr int LPT = TILEB / (W * 64 * 16);  // Q DMA instructions per wave per tile
+  constexpr int CB = W * ROWS * 4;            // -c2/c1 copies, one per wave
+  static_assert(NBUF >= 2 && NBUF <= 4 && LPT >= 1, "ring shape");
+  __shared__ __attribute__((aligned(16))) uint8_t q0[TILEB], q1[TILEB];
+  __shared__ __attribute__((aligned(16))) uint8_t q2[NBUF > 2 ? TILEB : 16], q3[NBUF > 3 ? TILEB : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t cs0[CB], cs1[CB];
+  __shared__ __attribute__((aligned(16))) uint8_t cs2[NBUF > 2 ? CB : 16], cs3[NBUF > 3 ? CB : 16];
+  auto qring = [&](int i) __attribute__((always_inline)) -> uint8_t* {
+    return i == 0 ? q0 : i == 1 ? q1 : i == 2 ? q2 : q3;
+  };
+  auto cring = [&](int i) __attribute__((always_inline)) -> uint8_t* {
+    return i == 0 ? cs0 : i == 1 ? cs1 : i == 2 ? cs2 : cs3;
+  };
 
   const int64_t tau = xcd_remap(blockIdx.x, gridDim.x);
   if (tau >= a.n_logical) return;
@@ -303,10 +335,10 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_bf16(P2Args a) {
   const int64_t r = t2 % a.R;
   const int64_t unit = t2 / a.R;
   const int64_t l = unit / a.Hkv, g = unit % a.Hkv;
-  const int64_t c0 = a.S + r * a.m;
-  const int64_t c1e = min(c0 + a.m, a.N);
-  const int64_t kt0 = c0 + tile * kP2Keys;
-  if (kt0 >= c1e) return;  // uniform over the workgroup, before any barrier
+  const int64_t cb0 = a.S + r * a.m;
+  const int64_t cb1 = min(cb0 + a.m, a.N);
+  const int64_t kt0 = cb0 + tile * (W * 64);
+  if (kt0 >= cb1) return;  // uniform over the workgroup, before any barrier
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
@@ -316,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_bf16(P2Args a) {
 
   if (r == 0 && tile == 0) {
     const int64_t ns = min(a.S, a.N);
-    for (int64_t i = tid; i < ns; i += kThreads) srow[i] = 1.0f;
+    for (int64_t i = tid; i < ns; i += W * 64) srow[i] = 1.0f;
   }
 
   bf16x8 kf[2][KS];
@@ -330,83 +362,130 @@ __global__ __launch_bounds__(kThreads, 2) void pass2_bf16(P2Args a) {
   }
 
   const int64_t unit_row0 = (l * a.Hq + g * a.G) * a.Nq;
-  const uint16_t* qunit = a.q + unit_row0 * D;
-  const int64_t nrows = (int64_t)a.G * a.nq;
+  const int64_t rows_per_unit = (int64_t)a.G * a.Nq;
+  const uint32_t nrows = (uint32_t)(a.G * a.nq);
   const int64_t ntiles = ceil_div(nrows, ROWS);
-  float cm[2] = {-INFINITY, -INFINITY};
+  const int64_t ngroups = ceil_div(ntiles, NBUF);
 
-  u32x4 pre[LOADS];
-  float cpre = INFINITY;
-  // unit row of chunk-row rho: head rho / nq of the group, query rho % nq of chunk r
+  // Buffer resources over the unit's query rows and their -c2/c1 values.
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.q + unit_row0 * D), (short)0, (int)(uint32_t)(rows_per_unit * ROWB),
+      kBufferFlags);
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.c2n + unit_row0), (short)0, (int)(uint32_t)(rows_per_unit * 4),
+      kBufferFlags);
+  // Unit row of chunk row rho (clamped to the chunk's last row): head rho / nq
+  // of the group, query rho % nq of chunk r.
   const uint32_t nq32 = (uint32_t)a.nq;
-  auto urow_of = [&](int64_t rho) __attribute__((always_inline)) -> int64_t {
-    const uint32_t x = (uint32_t)rho;
-    const uint32_t t = (__umulhi(x, a.nq_mul) + x) >> a.nq_shift;
-    return (int64_t)t * a.Nq + r * a.nq + (x - t * nq32);
+  const uint32_t rbase = (uint32_t)(r * a.nq);
+  auto urow = [&](uint32_t rho) __attribute__((always_inline)) -> uint32_t {
+    rho = min(rho, nrows - 1);
+    const uint32_t t = (__umulhi(rho, a.nq_mul) + rho) >> a.nq_shift;
+    return t * (uint32_t)a.Nq + rbase + (rho - t * nq32);
   };
-  auto gload = [&](int64_t tl) __attribute__((always_inline)) {
-    const int64_t base = tl * ROWS;
+  // Tile layout in LDS as in pass 1: row rr, 16-byte chunk c at
+  // rr*ROWB + ((c ^ (rr % CPR)) * 16).  Wave w's i-th DMA fills LDS chunks
+  // [(i*W + w)*64, +64) lane by lane; each lane fetches the chunk landing there.
+  auto dma = [&](uint8_t* qb, uint8_t* cb, int64_t tl) __attribute__((always_inline)) {
+    const uint32_t row0 = (uint32_t)(tl * ROWS);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + i * kThreads;
-      const int64_t rho = base + c / PIECES;
-      if (rho < nrows) {
-        pre[i] = *(const u32x4*)(qunit + urow_of(rho) * D + (c % PIECES) * 8);
-      } else {
-        pre[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < LPT; ++i) {
+      const int L = (i * W + wave) * 64 + lane;
+      const int rr = L / CPR;
+      const int cc = (L % CPR) ^ (rr & (CPR - 1));
+      const uint32_t off = urow(row0 + rr) * ROWB + cc * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, lds_ptr(qb + (i * W + wave) * 1024), 16, (int)off,
+                                               0, 0, 0);
     }
-    if (tid < ROWS) {
-      const int64_t rho = base + tid;
-      cpre = (rho < nrows) ? a.c2[unit_row0 + urow_of(rho)] : INFINITY;
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, lds_ptr(cb + wave * ROWS * 4), 4,
+                                             (int)(urow(row0 + lane) * 4), 0, 0, 0);
   };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
+  auto afrag = [&](const uint8_t* qb, int rb, int ks) __attribute__((always_inline)) -> bf16x8 {
+    const int row = rb * 32 + col;
+    const int c = 2 * ks + half;
+    return *(const bf16x8*)(qb + row * ROWB + ((c ^ (row & (CPR - 1))) * 16));
+  };
+  // -c2/c1 of the accumulator rows of stage rb: rows rb*32 + (i/4)*8 + half*4 + i%4.
+  auto cinit = [&](const uint8_t* cb, int rb) __attribute__((always_inline)) -> f32x16 {
+    const float* cw = reinterpret_cast<const float*>(cb + wave * ROWS * 4) + rb * 32 + half * 4;
+    f32x16 v;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int c = tid + i * kThreads;
-      *(u32x4*)(&sq[buf][(c / PIECES) * LD + (c % PIECES) * 8]) = pre[i];
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 x = *(const float4*)(cw + q4 * 8);
+      v[q4 * 4 + 0] = x.x;
+      v[q4 * 4 + 1] = x.y;
+      v[q4 * 4 + 2] = x.z;
+      v[q4 * 4 + 3] = x.w;
     }
-    if (tid < ROWS) sc[buf][tid] = cpre;
+    return v;
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int64_t t = 0; t < ntiles; ++t) {
-    const int buf = (int)(t & 1);
-    if (t + 1 < ntiles) gload(t + 1);
+  float cm[2] = {-INFINITY, -INFINITY};
+  f32x16 p0, p1;  // accumulators of the previous stage
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    p0[i] = -INFINITY;
+    p1[i] = -INFINITY;
+  }
+  auto compute_tile = [&](const uint8_t* qb, const uint8_t* cb) __attribute__((always_inline)) {
+    bf16x8 av[2][KS];
+    f32x16 ci[2];
+    ci[0] = cinit(cb, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) av[0][ks] = afrag(qb, 0, ks);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      f32x16 ci;
+      f32x16 x0 = ci[rb], x1 = ci[rb];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ci[i] = -sc[buf][rb * 32 + acc_row(i, lane)] * a.inv_c1;
-      const uint16_t* arow = &sq[buf][(rb * 32 + col) * LD + half * 8];
-      f32x16 acc0 = ci, acc1 = ci;
+      for (int i = 0; i < 2 * KS; ++i) {
+        const int ks = i >> 1;
+        if ((i & 1) == 0) {
+          x0 = mfma32x32x16(av[rb][ks], kf[0][ks], x0);
+        } else {
+          x1 = mfma32x32x16(av[rb][ks], kf[1][ks], x1);
+          if (rb == 0) av[1][ks] = afrag(qb, 1, ks);
+        }
+        if (rb == 0 && i == 0) ci[1] = cinit(cb, 1);
+        // running max over the previous stage, two elements per slot
+        constexpr int PER = 32 / (2 * KS);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 av = *(const bf16x8*)(arow + ks * 16);
-        acc0 = mfma32x32x16(av, kf[0][ks], acc0);
-        acc1 = mfma32x32x16(av, kf[1][ks], acc1);
+        for (int e = 0; e < PER; e += 2) {
+          const int j = i * PER + e;
+          if (j < 16) cm[0] = max3f(cm[0], p0[j], p0[j + 1]);
+          else cm[1] = max3f(cm[1], p1[j - 16], p1[j - 15]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      float m0 = max3f(max3f(acc0[0], acc0[1], acc0[2]), max3f(acc0[3], acc0[4], acc0[5]),
-                       max3f(acc0[6], acc0[7], acc0[8]));
-      m0 = max3f(m0, max3f(acc0[9], acc0[10], acc0[11]), max3f(acc0[12], acc0[13], acc0[14]));
-      cm[0] = max3f(cm[0], m0, acc0[15]);
-      float m1 = max3f(max3f(acc1[0], acc1[1], acc1[2]), max3f(acc1[3], acc1[4], acc1[5]),
-                       max3f(acc1[6], acc1[7], acc1[8]));
-      m1 = max3f(m1, max3f(acc1[9], acc1[10], acc1[11]), max3f(acc1[12], acc1[13], acc1[14]));
-      cm[1] = max3f(cm[1], m1, acc1[15]);
+      p0 = x0;
+      p1 = x1;
     }
-    if (t + 1 < ntiles) sstore(buf ^ 1);
-    __syncthreads();
+  };
+  // Tile u lives in ring slot u % NBUF; the ordering argument is that of pass 1.
+  auto step = [&](int b, int64_t u) __attribute__((always_inline)) {
+    wait_vmcnt<(NBUF - 2) * (LPT + 1)>();
+    __builtin_amdgcn_s_barrier();
+    dma(qring((b + NBUF - 1) % NBUF), cring((b + NBUF - 1) % NBUF), u + NBUF - 1);
+    compute_tile(qring(b), cring(b));
+  };
+
+#pragma unroll
+  for (int b = 0; b + 1 < NBUF; ++b) dma(qring(b), cring(b), b);
+  for (int64_t gi = 0; gi < ngroups; ++gi) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) step(b, gi * NBUF + b);
   }
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    cm[0] = max3f(cm[0], p0[j], p0[j + 1]);
+    cm[1] = max3f(cm[1], p1[j], p1[j + 1]);
+  }
+  wait_vmcnt<0>();  // no DMA may still target LDS when the workgroup exits
 
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const float v = fmaxf(cm[kb], swap_halves(cm[kb]));
     const int64_t key = kw + kb * 32 + col;
-    if (half == 0 && key < c1e) srow[key] = fminf(exp2_hw(v * a.c1), 1.0f);
+    if (half == 0 && key < cb1) srow[key] = fminf(exp2_hw(v * a.c1), 1.0f);
   }
 }
 
@@ -436,7 +515,7 @@ int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
   P1Args a1;
   a1.q = static_cast<const uint16_t*>(q);
   a1.k = static_cast<const uint16_t*>(k);
-  a1.c2 = c2;
+  a1.c2n = c2;
   a1.part_m = pm;
   a1.part_l = plw;
   a1.Nq = pl.n_queries;
@@ -452,22 +531,23 @@ int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
   a1.Hkv = p.kv_heads;
   a1.G = p.q_heads / p.kv_heads;
   a1.c1 = c1;
+  a1.inv_c1 = inv_c1;
   {
     TraceScope ts("score_pass1_bf16", st);
-    hipLaunchKernelGGL(pass1_bf16<D>, dim3((unsigned)pad8(a1.n_logical)), dim3(kThreads), 0, st, a1);
+    hipLaunchKernelGGL((pass1_bf16<D, kP1Keys, kP1Ring>), dim3((unsigned)pad8(a1.n_logical)), dim3(kThreads), 0, st, a1);
   }
   if (hipError_t e = hipGetLastError()) return (int)e;
   if (pl.splits > 1) {
     TraceScope ts("score_merge_splits", st);
     hipLaunchKernelGGL(merge_splits, dim3((unsigned)ceil_div(pl.total_rows, kThreads)),
-                       dim3(kThreads), 0, st, pm, plw, c2, pl.total_rows, pl.splits);
+                       dim3(kThreads), 0, st, pm, plw, c2, pl.total_rows, pl.splits, inv_c1);
     if (hipError_t e = hipGetLastError()) return (int)e;
   }
 
   P2Args a2;
   a2.q = a1.q;
   a2.k = a1.k;
-  a2.c2 = c2;
+  a2.c2n = c2;
   a2.scores = scores;
   a2.Nq = pl.n_queries;
   a2.N = N;
@@ -482,11 +562,11 @@ int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
   a2.Hkv = p.kv_heads;
   a2.G = a1.G;
   a2.c1 = c1;
-  a2.inv_c1 = inv_c1;
   fast_div((uint32_t)p.q_per_chunk, &a2.nq_mul, &a2.nq_shift);
   {
     TraceScope ts("score_pass2_bf16", st);
-    hipLaunchKernelGGL(pass2_bf16<D>, dim3((unsigned)pad8(a2.n_logical)), dim3(kThreads), 0, st, a2);
+    hipLaunchKernelGGL((pass2_bf16<D, kP2Waves, kP2Ring>), dim3((unsigned)pad8(a2.n_logical)),
+                       dim3(kP2Waves * 64), 0, st, a2);
   }
   if (hipError_t e = hipGetLastError()) return (int)e;
   return 0;
