@@ -56,7 +56,7 @@ constexpr int kP1Keys = 128;      // keys per pass-1 LDS tile
 constexpr int kP1Ring = 2;        // pass-1 LDS tiles in flight
 constexpr int kP2Waves = 4;       // pass-2 waves per workgroup, 64 keys each
 constexpr int kP2Keys = kP2Waves * 64;  // keys per pass-2 workgroup
-constexpr int kP2Ring = 2;        // pass-2 LDS query tiles in flight
+constexpr int kP2Ring = 3;        // pass-2 LDS query tiles in flight
 constexpr int kMaxSplits = 64;
 
 }  // namespace kvs

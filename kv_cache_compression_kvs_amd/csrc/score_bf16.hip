@@ -23,6 +23,7 @@
 // tiles filled by direct global->LDS loads.  Pass 2 workgroup: 64 keys per
 // wave resident in VGPRs; the chunk's query rows (all heads of the group)
 // stream through a ring of LDS tiles together with their -c2/c1 values.
+#include <float.h>
 #include <math.h>
 
 #include "kvs_device.h"
@@ -97,8 +98,11 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
   const int64_t ntiles = ceil_div(nkeys, TK);
   const int64_t ngroups = nfull / NBUF;
 
-  float m[2] = {-INFINITY, -INFINITY};
-  float ls[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // Running max (base-2 units) and sum of 2^(z c1 - m) per query block.  The
+  // start value is finite so that the pipeline's empty first stage (all -inf)
+  // adds exactly zero; the first real block moves m off it.
+  float m[2] = {-FLT_MAX, -FLT_MAX};
+  float ls[2] = {0.f, 0.f};
   const float c1 = a.c1;
 
   // Tile layout in LDS: row r (a key), 16-byte chunk c at r*ROWB + ((c ^ (r % CPR)) * 16).
@@ -127,35 +131,33 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
     return *(const bf16x8*)(buf + row * ROWB + ((c ^ (row & (CPR - 1))) * 16));
   };
 
-  // The update of one query block split in two parts: the head finds the
-  // block max, moves the running max and rescales the partial sums; the
-  // element part adds 2^(z c1 - max) for elements [e0, e1).
-  auto update_head = [&](const f32x16& z, float& mref, float (&l4)[4]) -> float {
+  // Exact update by one block: move m to the block's max if larger, rescale
+  // the sum, add the block's terms.
+  auto update = [&](int qb, const f32x16& z) __attribute__((always_inline)) {
     float mx = max3f(max3f(z[0], z[1], z[2]), max3f(z[3], z[4], z[5]), max3f(z[6], z[7], z[8]));
     mx = max3f(mx, max3f(z[9], z[10], z[11]), max3f(z[12], z[13], z[14]));
     mx = fmaxf(mx, z[15]);
-    const float mn = fmaxf(mref, mx * c1);
-    const float msh = (mn == -INFINITY) ? 0.f : mn;
-    const float sc = exp2_hw(mref - msh);
+    const float mn = fmaxf(m[qb], mx * c1);
+    float t4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) l4[j] *= sc;
-    mref = mn;
-    return msh;
-  };
-  auto update_elems = [&](const f32x16& z, float (&l4)[4], float msh, int e0, int e1) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (e >= e0 && e < e1) l4[e & 3] += exp2_hw(fmaf(z[e], c1, -msh));
-  };
-  auto update = [&](int qb, const f32x16& z) __attribute__((always_inline)) {
-    const float msh = update_head(z, m[qb], ls[qb]);
-    update_elems(z, ls[qb], msh, 0, 16);
+    for (int e = 0; e < 16; ++e) t4[e & 3] += exp2_hw(fmaf(z[e], c1, -mn));
+    ls[qb] = ls[qb] * exp2_hw(m[qb] - mn) + ((t4[0] + t4[1]) + (t4[2] + t4[3]));
+    m[qb] = mn;
   };
 
   // Software pipeline over 32-key blocks: the MFMAs of block j and the
   // softmax update of block j-1 sit in one basic block; after each MFMA one
   // slice of the update follows and a scheduling fence keeps that order, so
   // the vector ALU works while the MFMA occupies the matrix pipe.
+  //
+  // The update in the pipeline takes a block's terms against the current m
+  // without first reducing the block's max: one fma, one exp2 and one add per
+  // element.  A block sum below 2^16 proves that no term overflowed, and
+  // terms up to that size lose nothing in fp32; a block that fails the test
+  // (its max lies more than 16 above m, or it is the first block) takes a
+  // wave-uniform branch that redoes it exactly against its max.
+  // c2 = m + log2(l) is exact for any m, so this changes nothing but rounding.
+  constexpr float kSumLimit = 65536.f;
   f32x16 p0, p1;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
   }
   auto compute_tile = [&](const uint8_t* buf) __attribute__((always_inline)) {
     constexpr int NS = 2 * KS;      // MFMAs (and update slices) per block
-    constexpr int HALF = NS / 2;    // slices per query block
+    constexpr int EPS = 16 / NS;    // elements per slice of each query block
     bf16x8 af[2][KS];               // fragments of the current and the next key block
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) af[0][ks] = afrag(buf, 0, ks);
@@ -172,7 +174,8 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
     for (int kb = 0; kb < NB; ++kb) {
       const int cur = kb & 1;
       f32x16 n0 = {}, n1 = {};
-      float ms0 = 0.f, ms1 = 0.f;
+      float t0 = 0.f, t1 = 0.f;
+      const float m0 = m[0], m1 = m[1];
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         if ((i & 1) == 0) {
@@ -183,11 +186,19 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
           // next block's fragment ks now, so that block starts without an LDS wait
           if (kb + 1 < NB) af[cur ^ 1][i >> 1] = afrag(buf, kb + 1, i >> 1);
         }
-        if (i == 0) ms0 = update_head(p0, m[0], ls[0]);
-        else if (i < HALF) update_elems(p0, ls[0], ms0, 16 * (i - 1) / (HALF - 1), 16 * i / (HALF - 1));
-        else if (i == HALF) ms1 = update_head(p1, m[1], ls[1]);
-        else update_elems(p1, ls[1], ms1, 16 * (i - HALF - 1) / (HALF - 1), 16 * (i - HALF) / (HALF - 1));
+#pragma unroll
+        for (int u = 0; u < EPS; ++u) {
+          t0 += exp2_hw(fmaf(p0[i * EPS + u], c1, -m0));
+          t1 += exp2_hw(fmaf(p1[i * EPS + u], c1, -m1));
+        }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if (__any(!(t0 < kSumLimit) || !(t1 < kSumLimit))) {
+        update(0, p0);
+        update(1, p1);
+      } else {
+        ls[0] += t0;
+        ls[1] += t1;
       }
       p0 = n0;
       p1 = n1;
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float lsum = (ls[qb][0] + ls[qb][1]) + (ls[qb][2] + ls[qb][3]);
+    const float lsum = ls[qb];
     const float mo = swap_halves(m[qb]);
     const float lo = swap_halves(lsum);
     const float M = fmaxf(m[qb], mo);
@@ -316,7 +327,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pass2_bf16(P2Args a) {
   constexpr int TILEB = ROWS * ROWB;
   constexpr int LPT = TILEB / (W * 64 * 16);  // Q DMA instructions per wave per tile
   constexpr int CB = W * ROWS * 4;            // -c2/c1 copies, one per wave
-  static_assert(NBUF >= 2 && NBUF <= 4 && LPT >= 1, "ring shape");
+  static_assert(NBUF >= 3 && NBUF <= 4 && LPT >= 1, "ring shape");
   __shared__ __attribute__((aligned(16))) uint8_t q0[TILEB], q1[TILEB];
   __shared__ __attribute__((aligned(16))) uint8_t q2[NBUF > 2 ? TILEB : 16], q3[NBUF > 3 ? TILEB : 16];
   __shared__ __attribute__((aligned(16))) uint8_t cs0[CB], cs1[CB];
@@ -333,7 +344,10 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pass2_bf16(P2Args a) {
   const int64_t tile = tau % a.tiles;
   const int64_t t2 = tau / a.tiles;
   const int64_t r = t2 % a.R;
-  const int64_t unit = t2 / a.R;
+  // Units in reverse order: pass 1 streams the keys unit by unit in forward
+  // order just before, so the last units' keys are the ones still in the
+  // memory-side cache when this pass starts.
+  const int64_t unit = a.n_logical / (a.R * a.tiles) - 1 - t2 / a.R;
   const int64_t l = unit / a.Hkv, g = unit % a.Hkv;
   const int64_t cb0 = a.S + r * a.m;
   const int64_t cb1 = min(cb0 + a.m, a.N);
@@ -427,52 +441,67 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pass2_bf16(P2Args a) {
     p0[i] = -INFINITY;
     p1[i] = -INFINITY;
   }
-  auto compute_tile = [&](const uint8_t* qb, const uint8_t* cb) __attribute__((always_inline)) {
-    bf16x8 av[2][KS];
-    f32x16 ci[2];
-    ci[0] = cinit(cb, 0);
+  // One stage: 16 MFMAs on the fragments `av` with accumulators starting at
+  // `ci`, the running max over the previous stage interleaved, and the next
+  // stage's fragments fetched (`next(ks)` after fragment ks is dead, `cnext`
+  // after the first MFMA) so that stage starts without an LDS wait.
+  auto stage = [&](const bf16x8 (&av)[KS], const f32x16& ci, auto&& next, auto&& cnext)
+      __attribute__((always_inline)) {
+    f32x16 x0 = ci, x1 = ci;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) av[0][ks] = afrag(qb, 0, ks);
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      f32x16 x0 = ci[rb], x1 = ci[rb];
-#pragma unroll
-      for (int i = 0; i < 2 * KS; ++i) {
-        const int ks = i >> 1;
-        if ((i & 1) == 0) {
-          x0 = mfma32x32x16(av[rb][ks], kf[0][ks], x0);
-        } else {
-          x1 = mfma32x32x16(av[rb][ks], kf[1][ks], x1);
-          if (rb == 0) av[1][ks] = afrag(qb, 1, ks);
-        }
-        if (rb == 0 && i == 0) ci[1] = cinit(cb, 1);
-        // running max over the previous stage, two elements per slot
-        constexpr int PER = 32 / (2 * KS);
-#pragma unroll
-        for (int e = 0; e < PER; e += 2) {
-          const int j = i * PER + e;
-          if (j < 16) cm[0] = max3f(cm[0], p0[j], p0[j + 1]);
-          else cm[1] = max3f(cm[1], p1[j - 16], p1[j - 15]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < 2 * KS; ++i) {
+      const int ks = i >> 1;
+      if ((i & 1) == 0) {
+        x0 = mfma32x32x16(av[ks], kf[0][ks], x0);
+      } else {
+        x1 = mfma32x32x16(av[ks], kf[1][ks], x1);
+        next(ks);
       }
-      p0 = x0;
-      p1 = x1;
+      if (i == 0) cnext();
+      constexpr int PER = 32 / (2 * KS);
+#pragma unroll
+      for (int e = 0; e < PER; e += 2) {
+        const int j = i * PER + e;
+        if (j < 16) cm[0] = max3f(cm[0], p0[j], p0[j + 1]);
+        else cm[1] = max3f(cm[1], p1[j - 16], p1[j - 15]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  // Tile u lives in ring slot u % NBUF; the ordering argument is that of pass 1.
-  auto step = [&](int b, int64_t u) __attribute__((always_inline)) {
-    wait_vmcnt<(NBUF - 2) * (LPT + 1)>();
-    __builtin_amdgcn_s_barrier();
-    dma(qring((b + NBUF - 1) % NBUF), cring((b + NBUF - 1) % NBUF), u + NBUF - 1);
-    compute_tile(qring(b), cring(b));
+    p0 = x0;
+    p1 = x1;
   };
 
+  // Tile u lives in ring slot u % NBUF and is two stages (rows 0-31, 32-63).
+  // The barrier sits between the stages of tile u: after it every wave's
+  // loads of tile u+1 have landed (they were issued a tile earlier) and every
+  // wave is done with tile u-1, whose slot then takes the loads of tile
+  // u + NBUF - 1.  Stage 1 of tile u fetches stage 0 of tile u+1.  Rows past
+  // the last tile repeat the chunk's last row, so the tile count is padded to
+  // a multiple of NBUF.
+  bf16x8 avA[KS], avB[KS];
+  f32x16 ciA, ciB;
 #pragma unroll
   for (int b = 0; b + 1 < NBUF; ++b) dma(qring(b), cring(b), b);
+  wait_vmcnt<(NBUF - 2) * (LPT + 1)>();
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) avA[ks] = afrag(q0, 0, ks);
+  ciA = cinit(cs0, 0);
   for (int64_t gi = 0; gi < ngroups; ++gi) {
 #pragma unroll
-    for (int b = 0; b < NBUF; ++b) step(b, gi * NBUF + b);
+    for (int b = 0; b < NBUF; ++b) {
+      const uint8_t* qb = qring(b);
+      const uint8_t* cb = cring(b);
+      const uint8_t* qn = qring((b + 1) % NBUF);
+      const uint8_t* cn = cring((b + 1) % NBUF);
+      stage(avA, ciA, [&](int ks) __attribute__((always_inline)) { avB[ks] = afrag(qb, 1, ks); },
+            [&]() __attribute__((always_inline)) { ciB = cinit(cb, 1); });
+      wait_vmcnt<(NBUF - 3) * (LPT + 1)>();
+      __builtin_amdgcn_s_barrier();
+      dma(qring((b + NBUF - 1) % NBUF), cring((b + NBUF - 1) % NBUF), gi * NBUF + b + NBUF - 1);
+      stage(avB, ciB, [&](int ks) __attribute__((always_inline)) { avA[ks] = afrag(qn, 0, ks); },
+            [&]() __attribute__((always_inline)) { ciA = cinit(cn, 0); });
+    }
   }
 #pragma unroll
   for (int j = 0; j < 16; j += 2) {
