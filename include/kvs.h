@@ -211,6 +211,11 @@ typedef struct kvs_trace_entry {
 
 int kvs_trace_enable(int on);
 
+/* Restricts recording to launches whose kernel name (as reported by
+ * kvs_trace_summary, e.g. "score_pass1_bf16") equals `name`; NULL or "" records
+ * every launch again.  The string is copied.  Always returns KVS_OK. */
+int kvs_trace_only(const char* name);
+
 /* Writes up to max_entries entries to out (host) and the number of distinct
  * kernels seen to *n_entries.  Blocks until the recorded events complete. */
 int kvs_trace_summary(kvs_trace_entry* out, int max_entries, int* n_entries);

@@ -64,6 +64,7 @@ SIGNATURES = {
     "kvs_append_rows": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_int64, c_int64,
                                   c_void_p, c_int64, c_int64, c_void_p]),
     "kvs_trace_enable": (c_int32, [c_int32]),
+    "kvs_trace_only": (c_int32, [ctypes.c_char_p]),
     "kvs_trace_summary": (c_int32, [ctypes.POINTER(KvsTraceEntry), c_int32,
                                     ctypes.POINTER(c_int32)]),
 }

@@ -177,6 +177,11 @@ def kvs_trace_enable(on: bool) -> None:
     _check(_lib.lib().kvs_trace_enable(1 if on else 0), "kvs_trace_enable")
 
 
+def kvs_trace_only(name: Optional[str]) -> None:
+    """Record only launches of kernel `name` (None: every launch)."""
+    _check(_lib.lib().kvs_trace_only(name.encode() if name else None), "kvs_trace_only")
+
+
 def kvs_trace_summary() -> dict:
     """{kernel name: {"count", "total_ms", "min_ms", "max_ms", "avg_ms"}}; clears the record."""
     cap = 64

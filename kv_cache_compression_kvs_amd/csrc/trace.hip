@@ -1,7 +1,8 @@
 // Per-kernel timing with HIP events (off by default).
 //
-// When enabled, every kernel launch of the library is bracketed by two events
-// recorded on the launch stream, so the elapsed time between them is that
+// When enabled, every kernel launch of the library (or only those of one
+// name, see kvs_trace_only) is bracketed by two events recorded on the launch
+// stream, so the elapsed time between them is that
 // launch's duration on the GPU.  kvs_trace_summary waits for the recorded
 // events, aggregates count / total / min / max per kernel name and returns the
 // events to a pool, so steady-state tracing creates no new events.
@@ -25,6 +26,7 @@ struct Rec {
 
 std::mutex g_mu;
 bool g_on = false;
+std::string g_only;  // record only launches of this name when not empty
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -43,7 +45,7 @@ hipEvent_t take() {
 
 TraceScope::TraceScope(const char* name, hipStream_t st) : name_(name), st_(st) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on) return;
+  if (!g_on || (!g_only.empty() && g_only != name_)) return;
   a_ = take();
   b_ = take();
   if (!a_ || !b_ || hipEventRecord(static_cast<hipEvent_t>(a_), st_) != hipSuccess) {
@@ -73,6 +75,12 @@ extern "C" {
 int kvs_trace_enable(int on) {
   std::lock_guard<std::mutex> lk(g_mu);
   g_on = on != 0;
+  return KVS_OK;
+}
+
+int kvs_trace_only(const char* name) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_only = name ? name : "";
   return KVS_OK;
 }
 
