@@ -183,6 +183,46 @@ int kvs_compress_block(const kvs_problem* p, const void* q, const void* k, const
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The cache of one compression split in two buffers, as in the block-prefill
+ * loop (EpiCache review, "방법: 3단계" (2), Fig. 1(b)) when the kept cache and
+ * the newly prefilled block are scored together without first copying the
+ * block behind the cache.  For every slab s = l * Hkv + g, cache row i is
+ *   row s * head_row_stride + i of k_head / v_head          for i < head_rows,
+ *   row s * tail_row_stride + tail_row0 + (i - head_rows)
+ *                                  of k_tail / v_tail        for i >= head_rows.
+ * Rows are head_dim elements of the problem's dtype; all four pointers are
+ * device memory, 16-byte aligned, and are read only.
+ */
+typedef struct kvs_kv_segments {
+  const void* k_head;
+  const void* v_head;
+  int64_t head_rows;
+  int64_t head_row_stride;
+  const void* k_tail;
+  const void* v_tail;
+  int64_t tail_row0;
+  int64_t tail_row_stride;
+} kvs_kv_segments;
+
+/*
+ * kvs_compress_block on a cache given as two segments (kvs_kv_segments).  The
+ * results are those of kvs_compress_block on the concatenated cache, bit for
+ * bit: the kept rows of both segments are gathered into k_out / v_out, which
+ * must overlap none of the four inputs.  p->kv_row_stride must be 0 (the
+ * strides come with the segments).  head_rows must lie in [0, N] and be a
+ * multiple of 8 unless it equals N; head_row_stride >= head_rows when
+ * head_rows > 0; tail_row0 >= 0 and tail_row_stride >= tail_row0 + N -
+ * head_rows when head_rows < N.  Errors as kvs_compress_block, with
+ * KVS_E_NULL for seg == NULL or a needed pointer and KVS_E_SHAPE for the
+ * constraints above.
+ */
+int kvs_compress_block_seg(const kvs_problem* p, const void* q, const kvs_kv_segments* seg,
+                           int64_t total_budget, const double* sens, double alpha,
+                           float* scores, int32_t* kept, void* k_out, void* v_out,
+                           int64_t out_row_stride, int64_t* k_per_layer_out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Block append for the block-prefill loop (EpiCache review, "방법: 3단계" (2),
  * Fig. 1(b)): for each of `slabs` (layer, KV head) slabs copies rows
  * [src_row0, src_row0 + n_rows) of src (slab stride src_row_stride rows) to

@@ -3,8 +3,10 @@
 The computation lives in libkvs.so (HIP kernels behind the C ABI of
 include/kvs.h); this package only marshals arguments and sequences calls.
 """
-from ._lib import KVS_BF16, KVS_F32, KvsLibraryMissing, KvsProblem, LIB_PATH  # noqa: F401
+from ._lib import (KVS_BF16, KVS_F32, KvsKvSegments, KvsLibraryMissing,  # noqa: F401
+                   KvsProblem, LIB_PATH)
 from .api import (KvsError, kvs_append_rows, kvs_check_problem, kvs_compact,  # noqa: F401
-                  kvs_compress_block, kvs_layer_budgets, kvs_num_chunks, kvs_num_queries,
-                  kvs_score, kvs_select, kvs_status_string, kvs_trace_enable, kvs_trace_only,
-                  kvs_trace_summary, kvs_version, kvs_workspace_bytes, make_problem, workspace)
+                  kvs_compress_block, kvs_compress_block_seg, kvs_layer_budgets,
+                  kvs_num_chunks, kvs_num_queries, kvs_score, kvs_select, kvs_status_string,
+                  kvs_trace_enable, kvs_trace_only, kvs_trace_summary, kvs_version,
+                  kvs_workspace_bytes, make_problem, workspace)

@@ -33,6 +33,13 @@ class KvsProblem(ctypes.Structure):
                 ("dtype", c_int32), ("flags", c_int32)]
 
 
+class KvsKvSegments(ctypes.Structure):
+    """Mirror of struct kvs_kv_segments."""
+    _fields_ = [("k_head", c_void_p), ("v_head", c_void_p), ("head_rows", c_int64),
+                ("head_row_stride", c_int64), ("k_tail", c_void_p), ("v_tail", c_void_p),
+                ("tail_row0", c_int64), ("tail_row_stride", c_int64)]
+
+
 class KvsTraceEntry(ctypes.Structure):
     """Mirror of struct kvs_trace_entry."""
     _fields_ = [("name", ctypes.c_char * 48), ("count", c_int64), ("total_ms", c_double),
@@ -61,6 +68,10 @@ SIGNATURES = {
     "kvs_compress_block": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p, c_void_p, c_void_p,
                                      c_int64, P_F64, c_double, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_int64, P_I64, c_void_p, c_size_t, c_void_p]),
+    "kvs_compress_block_seg": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p,
+                                         ctypes.POINTER(KvsKvSegments), c_int64, P_F64, c_double,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_int64, P_I64,
+                                         c_void_p, c_size_t, c_void_p]),
     "kvs_append_rows": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_int64, c_int64,
                                   c_void_p, c_int64, c_int64, c_void_p]),
     "kvs_trace_enable": (c_int32, [c_int32]),

@@ -157,6 +157,28 @@ def kvs_compress_block(p: KvsProblem, q: Tensorish, k: Tensorish, v: Tensorish, 
     return np.array(kl[:], dtype=np.int64)
 
 
+def kvs_compress_block_seg(p: KvsProblem, q: Tensorish, k_head: Tensorish, v_head: Tensorish,
+                           head_rows: int, head_row_stride: int, k_tail: Tensorish,
+                           v_tail: Tensorish, tail_row0: int, tail_row_stride: int,
+                           total_budget: int, sens: Optional[Sequence[float]], alpha: float,
+                           scores: Tensorish, kept: Tensorish, k_out: Tensorish,
+                           v_out: Tensorish, out_row_stride: int = 0, ws: Tensorish = None,
+                           ws_bytes: Optional[int] = None, stream=None) -> np.ndarray:
+    """kvs_compress_block on a cache held as two segments; returns the per-layer budgets."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    seg = _lib.KvsKvSegments(_dev(k_head, "k_head"), _dev(v_head, "v_head"), head_rows,
+                             head_row_stride, _dev(k_tail, "k_tail"), _dev(v_tail, "v_tail"),
+                             tail_row0, tail_row_stride)
+    kl = (ctypes.c_int64 * p.layers)()
+    _check(_lib.lib().kvs_compress_block_seg(
+        ctypes.byref(p), _dev(q, "q"), ctypes.byref(seg), total_budget, _f64(sens),
+        float(alpha), _dev(scores, "scores"), _dev(kept, "kept"), _dev(k_out, "k_out"),
+        _dev(v_out, "v_out"), out_row_stride, kl, _dev(ws, "ws"), ws_bytes, _stream(stream)),
+        "kvs_compress_block_seg")
+    return np.array(kl[:], dtype=np.int64)
+
+
 def kvs_append_rows(slabs: int, head_dim: int, dtype: Union[int, torch.dtype], src: Tensorish,
                     src_row_stride: int, src_row0: int, n_rows: int, dst: Tensorish,
                     dst_row_stride: int, dst_row0: int, stream=None) -> None:

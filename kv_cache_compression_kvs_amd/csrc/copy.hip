@@ -22,12 +22,14 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 
 struct CompactArgs {
-  const uint8_t* k;
-  const uint8_t* v;
+  const uint8_t* kh;  // rows [0, split) of each slab, slab stride h_stride rows
+  const uint8_t* vh;
+  const uint8_t* kt;  // rows [split, n_cache): row t_row0 + (i - split), slab stride t_stride
+  const uint8_t* vt;
   const int32_t* kept;
   uint8_t* ko;
   uint8_t* vo;
-  int64_t row_bytes, kv_stride, out_stride, n_cache;
+  int64_t row_bytes, h_stride, t_stride, t_row0, split, out_stride, n_cache;
   int32_t Hkv;
   LayerTable t;
 };
@@ -41,9 +43,9 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   const int64_t t0 = (int64_t)blockIdx.x * (RPP * kUnroll);
   if (t0 >= kl) return;
   const int32_t* kp = a.kept + a.t.off[l] + g * kl;
-  const int64_t slab = (l * a.Hkv + g) * a.kv_stride * a.row_bytes;
-  const uint8_t* ks = a.k + slab;
-  const uint8_t* vs = a.v + slab;
+  const int64_t slab = l * a.Hkv + g;
+  const int64_t hoff = slab * a.h_stride * a.row_bytes;
+  const int64_t toff = (slab * a.t_stride + a.t_row0 - a.split) * a.row_bytes;  // + i * row_bytes
   const int64_t orow0 = a.out_stride ? (l * a.Hkv + g) * a.out_stride : a.t.off[l] + g * kl;
   uint8_t* ko = a.ko + orow0 * a.row_bytes;
   uint8_t* vo = a.vo + orow0 * a.row_bytes;
@@ -60,9 +62,11 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     ok[u] = t0 + u * RPP + rsub < kl && idx[u] >= 0 && idx[u] < a.n_cache;  // rows outside the cache are skipped
-    const int64_t src = (ok[u] ? idx[u] : 0) * a.row_bytes + piece * 16;
-    kb[u] = __builtin_nontemporal_load((const u32x4*)(ks + src));
-    vb[u] = __builtin_nontemporal_load((const u32x4*)(vs + src));
+    const int64_t i = ok[u] ? idx[u] : 0;
+    const bool head = i < a.split;
+    const int64_t src = (head ? hoff : toff) + i * a.row_bytes + piece * 16;
+    kb[u] = __builtin_nontemporal_load((const u32x4*)((head ? a.kh : a.kt) + src));
+    vb[u] = __builtin_nontemporal_load((const u32x4*)((head ? a.vh : a.vt) + src));
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
@@ -127,17 +131,22 @@ int append_lpr(int32_t slabs, int64_t row_bytes, const void* src, int64_t src_st
 
 }  // namespace
 
-int launch_compact(const kvs_problem& p, const void* k, const void* v, const int32_t* kept,
+int launch_compact(const kvs_problem& p, const KvSrc& kv, const int32_t* kept,
                    const LayerTable& t, int32_t k_max, void* k_out, void* v_out,
                    int64_t out_row_stride, void* stream) {
   CompactArgs a;
-  a.k = static_cast<const uint8_t*>(k);
-  a.v = static_cast<const uint8_t*>(v);
+  a.kh = static_cast<const uint8_t*>(kv.k_head);
+  a.vh = static_cast<const uint8_t*>(kv.v_head);
+  a.kt = static_cast<const uint8_t*>(kv.k_tail);
+  a.vt = static_cast<const uint8_t*>(kv.v_tail);
+  a.h_stride = kv.head_stride;
+  a.t_stride = kv.tail_stride;
+  a.t_row0 = kv.tail_row0;
+  a.split = kv.split;
   a.kept = kept;
   a.ko = static_cast<uint8_t*>(k_out);
   a.vo = static_cast<uint8_t*>(v_out);
   a.row_bytes = (int64_t)p.head_dim * (p.dtype == KVS_F32 ? 4 : 2);
-  a.kv_stride = p.kv_row_stride ? p.kv_row_stride : p.n_cache;
   a.out_stride = out_row_stride;
   a.n_cache = p.n_cache;
   a.Hkv = p.kv_heads;

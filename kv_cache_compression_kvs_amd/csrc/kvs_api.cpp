@@ -118,27 +118,91 @@ int build_table(const kvs_problem& p, const int64_t* kpl, bool for_select, int64
   return KVS_OK;
 }
 
-int do_score(const kvs_problem& p, const void* q, const void* k, float* scores, void* ws,
-             size_t ws_bytes) {
-  const ScorePlan pl = plan_score(p);
-  if (p.n_cache > 0 && (!k || !scores)) return KVS_E_NULL;
-  if (pl.n_queries > 0 && !q) return KVS_E_NULL;
-  if (pl.ws_bytes > 0 && !ws) return KVS_E_NULL;
-  if (ws_bytes < pl.ws_bytes) return KVS_E_WORKSPACE;
-  if ((q && !aligned(q, 16)) || (k && !aligned(k, 16)) || (scores && !aligned(scores, 4)) ||
-      (ws && !aligned(ws, 256)))
+// The single-buffer layout of K and V: rows [0, N) of each slab at stride
+// kv_row_stride (0: N).
+KvSrc single_src(const kvs_problem& p, const void* k, const void* v) {
+  KvSrc kv;
+  const int64_t stride = p.kv_row_stride ? p.kv_row_stride : p.n_cache;
+  kv.k_head = k;
+  kv.v_head = v;
+  kv.head_stride = stride;
+  kv.k_tail = k;
+  kv.v_tail = v;
+  kv.tail_stride = stride;
+  kv.tail_row0 = p.n_cache;
+  kv.split = p.n_cache;
+  return kv;
+}
+
+// Null and alignment checks of the buffers a call reads (V only if need_v).
+int check_src(const kvs_problem& p, const KvSrc& kv, bool need_v) {
+  if (p.n_cache == 0) return KVS_OK;
+  const bool head = kv.split > 0, tail = kv.split < p.n_cache;
+  if ((head && !kv.k_head) || (tail && !kv.k_tail)) return KVS_E_NULL;
+  if (need_v && ((head && !kv.v_head) || (tail && !kv.v_tail))) return KVS_E_NULL;
+  if ((head && !aligned(kv.k_head, 16)) || (tail && !aligned(kv.k_tail, 16))) return KVS_E_ALIGN;
+  if (need_v && ((head && !aligned(kv.v_head, 16)) || (tail && !aligned(kv.v_tail, 16))))
     return KVS_E_ALIGN;
   return KVS_OK;
 }
 
-int enqueue_score(const kvs_problem& p, const void* q, const void* k, float* scores, void* ws,
+int do_score(const kvs_problem& p, const void* q, const KvSrc& kv, float* scores, void* ws,
+             size_t ws_bytes) {
+  const ScorePlan pl = plan_score(p);
+  if (p.n_cache > 0 && !scores) return KVS_E_NULL;
+  if (int st = check_src(p, kv, false)) return st;
+  if (pl.n_queries > 0 && !q) return KVS_E_NULL;
+  if (pl.ws_bytes > 0 && !ws) return KVS_E_NULL;
+  if (ws_bytes < pl.ws_bytes) return KVS_E_WORKSPACE;
+  if ((q && !aligned(q, 16)) || (scores && !aligned(scores, 4)) || (ws && !aligned(ws, 256)))
+    return KVS_E_ALIGN;
+  return KVS_OK;
+}
+
+int enqueue_score(const kvs_problem& p, const void* q, const KvSrc& kv, float* scores, void* ws,
                   void* stream) {
   if (p.n_cache == 0) return KVS_OK;
   const ScorePlan pl = plan_score(p);
   if (pl.n_chunks == 0)  // every position is a sink
     return to_status(launch_fill(scores, (int64_t)p.layers * p.kv_heads * p.n_cache, 1.0f, stream));
-  if (p.dtype == KVS_BF16) return to_status(launch_score_bf16(p, pl, q, k, scores, ws, stream));
-  return to_status(launch_score_f32(p, pl, q, k, scores, ws, stream));
+  if (p.dtype == KVS_BF16) return to_status(launch_score_bf16(p, pl, q, kv, scores, ws, stream));
+  return to_status(launch_score_f32(p, pl, q, kv, scores, ws, stream));
+}
+
+// kvs_layer_budgets, kvs_score, kvs_select and kvs_compact in sequence, on a
+// problem check() has accepted.
+int compress(const kvs_problem& p, const void* q, const KvSrc& kv, int64_t total_budget,
+             const double* sens, double alpha, float* scores, int32_t* kept, void* k_out,
+             void* v_out, int64_t out_row_stride, int64_t* k_per_layer_out, void* ws,
+             size_t ws_bytes, void* stream) {
+  if (out_row_stride < 0) return KVS_E_SHAPE;
+  std::vector<int64_t> kl(p.layers);
+  int st;
+  if (total_budget >= (int64_t)p.layers * p.n_cache) {
+    std::fill(kl.begin(), kl.end(), p.n_cache);  // everything fits: copy through
+  } else {
+    st = budgets(p.layers, total_budget, sens, alpha, p.n_cache, p.n_sinks, kl.data());
+    if (st) return st;
+  }
+  LayerTable t;
+  int32_t kmax = 0;
+  st = build_table(p, kl.data(), true, out_row_stride, &t, &kmax);
+  if (st) return st;
+  st = do_score(p, q, kv, scores, ws, ws_bytes);
+  if (st) return st;
+  if ((st = check_src(p, kv, true))) return st;
+  if (p.n_cache > 0 && (!kept || !k_out || !v_out)) return KVS_E_NULL;
+  if ((kept && !aligned(kept, 4)) || (k_out && !aligned(k_out, 16)) ||
+      (v_out && !aligned(v_out, 16)))
+    return KVS_E_ALIGN;
+  if (k_per_layer_out) std::memcpy(k_per_layer_out, kl.data(), sizeof(int64_t) * p.layers);
+  if (p.n_cache == 0) return KVS_OK;
+  st = enqueue_score(p, q, kv, scores, ws, stream);
+  if (st) return st;
+  st = to_status(launch_select(p, scores, t, kept, stream));
+  if (st) return st;
+  if (kmax == 0) return KVS_OK;
+  return to_status(launch_compact(p, kv, kept, t, kmax, k_out, v_out, out_row_stride, stream));
 }
 
 }  // namespace
@@ -236,9 +300,10 @@ int kvs_score(const kvs_problem* p, const void* q, const void* k, float* scores,
               size_t ws_bytes, void* stream) {
   int st = check(p);
   if (st) return st;
-  st = do_score(*p, q, k, scores, ws, ws_bytes);
+  const KvSrc kv = single_src(*p, k, nullptr);
+  st = do_score(*p, q, kv, scores, ws, ws_bytes);
   if (st) return st;
-  return enqueue_score(*p, q, k, scores, ws, stream);
+  return enqueue_score(*p, q, kv, scores, ws, stream);
 }
 
 int kvs_select(const kvs_problem* p, const float* scores, const int64_t* k_per_layer,
@@ -271,7 +336,8 @@ int kvs_compact(const kvs_problem* p, const void* k, const void* v, const int32_
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
       !aligned(kept, 4))
     return KVS_E_ALIGN;
-  return to_status(launch_compact(*p, k, v, kept, t, kmax, k_out, v_out, out_row_stride, stream));
+  return to_status(launch_compact(*p, single_src(*p, k, v), kept, t, kmax, k_out, v_out,
+                                  out_row_stride, stream));
 }
 
 int kvs_compress_block(const kvs_problem* p, const void* q, const void* k, const void* v,
@@ -280,32 +346,36 @@ int kvs_compress_block(const kvs_problem* p, const void* q, const void* k, const
                        int64_t* k_per_layer_out, void* ws, size_t ws_bytes, void* stream) {
   int st = check(p);
   if (st) return st;
-  if (out_row_stride < 0) return KVS_E_SHAPE;
-  std::vector<int64_t> kl(p->layers);
-  if (total_budget >= (int64_t)p->layers * p->n_cache) {
-    std::fill(kl.begin(), kl.end(), p->n_cache);  // everything fits: copy through
-  } else {
-    st = budgets(p->layers, total_budget, sens, alpha, p->n_cache, p->n_sinks, kl.data());
-    if (st) return st;
-  }
-  LayerTable t;
-  int32_t kmax = 0;
-  st = build_table(*p, kl.data(), true, out_row_stride, &t, &kmax);
+  return compress(*p, q, single_src(*p, k, v), total_budget, sens, alpha, scores, kept, k_out,
+                  v_out, out_row_stride, k_per_layer_out, ws, ws_bytes, stream);
+}
+
+int kvs_compress_block_seg(const kvs_problem* p, const void* q, const kvs_kv_segments* seg,
+                           int64_t total_budget, const double* sens, double alpha,
+                           float* scores, int32_t* kept, void* k_out, void* v_out,
+                           int64_t out_row_stride, int64_t* k_per_layer_out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  int st = check(p);
   if (st) return st;
-  st = do_score(*p, q, k, scores, ws, ws_bytes);
-  if (st) return st;
-  if (p->n_cache > 0 && (!kept || !v || !k_out || !v_out)) return KVS_E_NULL;
-  if ((kept && !aligned(kept, 4)) || (v && !aligned(v, 16)) || (k_out && !aligned(k_out, 16)) ||
-      (v_out && !aligned(v_out, 16)))
-    return KVS_E_ALIGN;
-  if (k_per_layer_out) std::memcpy(k_per_layer_out, kl.data(), sizeof(int64_t) * p->layers);
-  if (p->n_cache == 0) return KVS_OK;
-  st = enqueue_score(*p, q, k, scores, ws, stream);
-  if (st) return st;
-  st = to_status(launch_select(*p, scores, t, kept, stream));
-  if (st) return st;
-  if (kmax == 0) return KVS_OK;
-  return to_status(launch_compact(*p, k, v, kept, t, kmax, k_out, v_out, out_row_stride, stream));
+  if (!seg) return KVS_E_NULL;
+  const int64_t N = p->n_cache;
+  const int64_t h = seg->head_rows;
+  if (p->kv_row_stride != 0) return KVS_E_SHAPE;  // strides come with the segments
+  if (h < 0 || h > N || (h % 8 != 0 && h != N)) return KVS_E_SHAPE;
+  if (h > 0 && seg->head_row_stride < h) return KVS_E_SHAPE;
+  if (h < N && (seg->tail_row0 < 0 || seg->tail_row_stride < seg->tail_row0 + (N - h)))
+    return KVS_E_SHAPE;
+  KvSrc kv;
+  kv.k_head = seg->k_head;
+  kv.v_head = seg->v_head;
+  kv.head_stride = seg->head_row_stride;
+  kv.k_tail = seg->k_tail;
+  kv.v_tail = seg->v_tail;
+  kv.tail_stride = seg->tail_row_stride;
+  kv.tail_row0 = seg->tail_row0;
+  kv.split = h;
+  return compress(*p, q, kv, total_budget, sens, alpha, scores, kept, k_out, v_out,
+                  out_row_stride, k_per_layer_out, ws, ws_bytes, stream);
 }
 
 int kvs_append_rows(int32_t slabs, int32_t head_dim, int32_t dtype, const void* src,

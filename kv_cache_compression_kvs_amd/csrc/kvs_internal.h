@@ -35,15 +35,30 @@ struct LayerTable {
 
 ScorePlan plan_score(const kvs_problem& p);
 
+// Where the cached rows live.  Row i of slab s = l * Hkv + g is row
+// s * head_stride + i of the head buffers for i < split, and row
+// s * tail_stride + tail_row0 + (i - split) of the tail buffers otherwise.
+// A single buffer is the case split = N (the tail is then never read).
+struct KvSrc {
+  const void* k_head = nullptr;
+  const void* v_head = nullptr;
+  int64_t head_stride = 0;
+  const void* k_tail = nullptr;
+  const void* v_tail = nullptr;
+  int64_t tail_stride = 0;
+  int64_t tail_row0 = 0;
+  int64_t split = 0;
+};
+
 // Launchers.  Each returns 0 on success or a nonzero HIP error code.
 int launch_score_bf16(const kvs_problem& p, const ScorePlan& pl, const void* q,
-                      const void* k, float* scores, void* ws, void* stream);
+                      const KvSrc& kv, float* scores, void* ws, void* stream);
 int launch_score_f32(const kvs_problem& p, const ScorePlan& pl, const void* q,
-                     const void* k, float* scores, void* ws, void* stream);
+                     const KvSrc& kv, float* scores, void* ws, void* stream);
 int launch_fill(float* dst, int64_t n, float value, void* stream);
 int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t,
                   int32_t* kept, void* stream);
-int launch_compact(const kvs_problem& p, const void* k, const void* v, const int32_t* kept,
+int launch_compact(const kvs_problem& p, const KvSrc& kv, const int32_t* kept,
                    const LayerTable& t, int32_t k_max, void* k_out, void* v_out,
                    int64_t out_row_stride, void* stream);
 int launch_append(int32_t slabs, int64_t row_bytes, const void* src, int64_t src_stride,

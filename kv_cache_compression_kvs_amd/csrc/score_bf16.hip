@@ -37,11 +37,13 @@ constexpr int kThreads = 256;
 
 struct P1Args {
   const uint16_t* q;
-  const uint16_t* k;
+  const uint8_t* kh;  // key rows [0, split) of each slab, slab stride kh_stride rows
+  const uint8_t* kt;  // key rows [split, N): row kt_row0 + (i - split), slab stride kt_stride
   float* c2n;       // [total_rows] -c2 / c1, written when splits == 1
   float* part_m;    // [splits][total_rows]
   float* part_l;    // [splits][total_rows]
-  int64_t Nq, N, kv_stride, rows_per_unit, row_blocks, splits, keys_per_split, total_rows;
+  int64_t Nq, N, rows_per_unit, row_blocks, splits, keys_per_split, total_rows;
+  int64_t kh_stride, kt_stride, kt_row0, split;
   int64_t n_logical;
   int32_t Hq, Hkv, G;
   float c1, inv_c1;
@@ -73,12 +75,15 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
   const int64_t unit = t2 / a.splits;
   const int64_t l = unit / a.Hkv, g = unit % a.Hkv;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps DMA operands scalar
   const int col = lane & 31, half = lane >> 5;
 
   const int64_t unit_row0 = (l * a.Hq + g * a.G) * a.Nq;
   const uint16_t* qunit = a.q + unit_row0 * D;
-  const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(a.k + (l * a.Hkv + g) * a.kv_stride * D);
+  const int64_t slab = l * a.Hkv + g;
+  const uint8_t* khead = a.kh + slab * a.kh_stride * ROWB;
+  const uint8_t* ktail = a.kt + (slab * a.kt_stride + a.kt_row0) * ROWB;
   const int64_t row_w = rb * kP1Rows + wave * 64;
 
   bf16x8 qf[2][KS];
@@ -108,22 +113,34 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
   // Tile layout in LDS: row r (a key), 16-byte chunk c at r*ROWB + ((c ^ (r % CPR)) * 16).
   // The XOR swizzle makes the fragment reads (32 rows, same chunk) hit
   // distinct banks.  Wave w's i-th DMA fills LDS chunks [(4i+w)*64, +64),
-  // lane by lane, so each lane fetches the global chunk that lands there.
-  // That chunk's byte offset inside the tile is the same for every i up to
-  // i * 4096 (r % CPR does not depend on i), so one offset register per lane
-  // serves every DMA and the tile position rides in the scalar offset.  The
-  // buffer resource covers rows [0, N) of this slab: rows past the end read
-  // as zero instead of leaving the slab.
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(kbytes), (short)0, (int)(uint32_t)(a.N * ROWB), kBufferFlags);
+  // that is RPI whole rows starting at row (4i+w)*RPI, lane by lane, so each
+  // lane fetches the global chunk that lands there.  The lane's part of the
+  // byte offset (its row within those RPI rows and its swizzled chunk) is the
+  // same for every i and w, because (4i+w)*RPI is a multiple of CPR or adds
+  // the same residue; the instruction's first row rides in the scalar
+  // offset.  That row also picks the buffer (head or tail segment: every
+  // segment boundary is a multiple of RPI), and each buffer resource covers
+  // exactly its segment's rows, so rows past the end read as zero instead of
+  // leaving the slab.
+  constexpr int RPI = 64 / CPR;
+  const __amdgpu_buffer_rsrc_t rs_head = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(khead), (short)0, (int)(uint32_t)(a.split * ROWB), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rs_tail = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(ktail), (short)0, (int)(uint32_t)((a.N - a.split) * ROWB), kBufferFlags);
   const int lrow = (wave * 64 + lane) / CPR;
-  const uint32_t voff = (uint32_t)(lrow * ROWB + (((wave * 64 + lane) % CPR) ^ (lrow & (CPR - 1))) * 16);
+  const uint32_t voff = (uint32_t)((lane / CPR) * ROWB + (((wave * 64 + lane) % CPR) ^ (lrow & (CPR - 1))) * 16);
   auto dma = [&](uint8_t* buf, int64_t tile) __attribute__((always_inline)) {
-    const uint32_t base = (uint32_t)((kbeg + tile * TK) * ROWB);
+    const int64_t row0 = kbeg + tile * TK;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lds_ptr(buf + (i * 4 + wave) * 1024), 16, (int)voff,
-                                               (int)(base + i * 4096), 0, 0);
+    for (int i = 0; i < LPT; ++i) {
+      const int64_t rf = row0 + (i * 4 + wave) * RPI;
+      auto* dst = lds_ptr(buf + (i * 4 + wave) * 1024);
+      if (rf < a.split)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_head, dst, 16, (int)voff, (int)(uint32_t)(rf * ROWB), 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_tail, dst, 16, (int)voff,
+                                                 (int)(uint32_t)((rf - a.split) * ROWB), 0, 0);
+    }
   };
   auto afrag = [&](const uint8_t* buf, int kb, int ks) __attribute__((always_inline)) -> bf16x8 {
     const int row = kb * 32 + col;
@@ -301,10 +318,12 @@ __global__ __launch_bounds__(kThreads) void merge_splits(const float* pm, const 
 
 struct P2Args {
   const uint16_t* q;
-  const uint16_t* k;
+  const uint16_t* kh;  // as in P1Args
+  const uint16_t* kt;
   const float* c2n;     // [total_rows] -c2 / c1 per query row
   float* scores;
-  int64_t Nq, N, S, m, nq, kv_stride, R, tiles, n_logical;
+  int64_t Nq, N, S, m, nq, R, tiles, n_logical;
+  int64_t kh_stride, kt_stride, kt_row0, split;
   int32_t Hq, Hkv, G;
   uint32_t nq_mul, nq_shift;  // rho / nq as (umulhi(rho, nq_mul) + rho) >> nq_shift
   float c1;
@@ -357,7 +376,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pass2_bf16(P2Args a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 31, half = lane >> 5;
   const int64_t kw = kt0 + wave * 64;
-  const uint16_t* kslab = a.k + (l * a.Hkv + g) * a.kv_stride * D;
+  const uint16_t* khead = a.kh + unit * a.kh_stride * D;
+  const uint16_t* ktail = a.kt + (unit * a.kt_stride + a.kt_row0) * D;
   float* srow = a.scores + unit * a.N;
 
   if (r == 0 && tile == 0) {
@@ -370,7 +390,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void pass2_bf16(P2Args a) {
   for (int kb = 0; kb < 2; ++kb) {
     int64_t key = kw + kb * 32 + col;
     if (key > a.N - 1) key = a.N - 1;
-    const uint16_t* src = kslab + key * D + half * 8;
+    const uint16_t* src = (key < a.split ? khead + key * D : ktail + (key - a.split) * D) + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = *(const bf16x8*)(src + ks * 16);
   }
@@ -530,26 +550,29 @@ inline void fast_div(uint32_t d, uint32_t* mul, uint32_t* shift) {
 inline int64_t pad8(int64_t n) { return (n + 7) & ~int64_t(7); }
 
 template <int D>
-int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k, float* scores,
+int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const KvSrc& kv, float* scores,
         void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   float* c2 = reinterpret_cast<float*>(w + pl.off_c2);
   float* pm = reinterpret_cast<float*>(w + pl.off_pm);
   float* plw = reinterpret_cast<float*>(w + pl.off_pl);
   const int64_t N = p.n_cache;
-  const int64_t stride = p.kv_row_stride ? p.kv_row_stride : N;
   const float c1 = (float)(1.4426950408889634 / sqrt((double)D));
   const float inv_c1 = (float)(sqrt((double)D) / 1.4426950408889634);
 
   P1Args a1;
   a1.q = static_cast<const uint16_t*>(q);
-  a1.k = static_cast<const uint16_t*>(k);
+  a1.kh = static_cast<const uint8_t*>(kv.k_head);
+  a1.kt = static_cast<const uint8_t*>(kv.k_tail);
+  a1.kh_stride = kv.head_stride;
+  a1.kt_stride = kv.tail_stride;
+  a1.kt_row0 = kv.tail_row0;
+  a1.split = kv.split;
   a1.c2n = c2;
   a1.part_m = pm;
   a1.part_l = plw;
   a1.Nq = pl.n_queries;
   a1.N = N;
-  a1.kv_stride = stride;
   a1.rows_per_unit = pl.rows_per_unit;
   a1.row_blocks = pl.row_blocks;
   a1.splits = pl.splits;
@@ -575,7 +598,12 @@ int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
 
   P2Args a2;
   a2.q = a1.q;
-  a2.k = a1.k;
+  a2.kh = static_cast<const uint16_t*>(kv.k_head);
+  a2.kt = static_cast<const uint16_t*>(kv.k_tail);
+  a2.kh_stride = kv.head_stride;
+  a2.kt_stride = kv.tail_stride;
+  a2.kt_row0 = kv.tail_row0;
+  a2.split = kv.split;
   a2.c2n = c2;
   a2.scores = scores;
   a2.Nq = pl.n_queries;
@@ -583,7 +611,6 @@ int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
   a2.S = p.n_sinks;
   a2.m = p.chunk_size;
   a2.nq = p.q_per_chunk;
-  a2.kv_stride = stride;
   a2.R = pl.n_chunks;
   a2.tiles = pl.p2_tiles;
   a2.n_logical = pl.units * pl.n_chunks * pl.p2_tiles;
@@ -603,11 +630,11 @@ int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
 
 }  // namespace
 
-int launch_score_bf16(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
+int launch_score_bf16(const kvs_problem& p, const ScorePlan& pl, const void* q, const KvSrc& kv,
                       float* scores, void* ws, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (p.head_dim == 128) return run<128>(p, pl, q, k, scores, ws, st);
-  return run<64>(p, pl, q, k, scores, ws, st);
+  if (p.head_dim == 128) return run<128>(p, pl, q, kv, scores, ws, st);
+  return run<64>(p, pl, q, kv, scores, ws, st);
 }
 
 }  // namespace kvs

@@ -21,25 +21,37 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Key rows of one slab: [0, split) at `head`, [split, N) at `tail` (row i at
+// tail + (i - split) * D).
+struct Keys {
+  const float* kh;
+  const float* kt;
+  int64_t kh_stride, kt_stride, kt_row0, split;
+};
+
+__device__ __forceinline__ const float* key_row(const Keys& k, int64_t slab, int64_t i, int D) {
+  return i < k.split ? k.kh + (slab * k.kh_stride + i) * D
+                     : k.kt + (slab * k.kt_stride + k.kt_row0 + (i - k.split)) * D;
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void pass1_f32(const float* __restrict__ q,
-                                                      const float* __restrict__ k,
+__global__ __launch_bounds__(kThreads) void pass1_f32(const float* __restrict__ q, Keys keys,
                                                       float* __restrict__ c2, int64_t total_rows,
-                                                      int64_t Nq, int64_t N, int64_t kv_stride,
-                                                      int32_t Hq, int32_t Hkv, float c1) {
+                                                      int64_t Nq, int64_t N, int32_t Hq,
+                                                      int32_t Hkv, float c1) {
   const int64_t row = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t rr = row < total_rows ? row : total_rows - 1;
   const int64_t h_all = rr / Nq;                 // l * Hq + h
   const int64_t l = h_all / Hq, h = h_all % Hq;
   const int64_t g = h / (Hq / Hkv);
   const float* qr = q + rr * D;
-  const float* ks = k + (l * Hkv + g) * kv_stride * D;
+  const int64_t slab = l * Hkv + g;
   float qv[D];
 #pragma unroll
   for (int t = 0; t < D; ++t) qv[t] = qr[t];
   float m = -INFINITY, s = 0.f;
   for (int64_t i = 0; i < N; ++i) {
-    const float* kr = ks + i * D;
+    const float* kr = key_row(keys, slab, i, D);
     float z0 = 0.f, z1 = 0.f, z2 = 0.f, z3 = 0.f;
 #pragma unroll
     for (int t = 0; t < D; t += 4) {
@@ -60,14 +72,12 @@ __global__ __launch_bounds__(kThreads) void pass1_f32(const float* __restrict__ 
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void pass2_f32(const float* __restrict__ q,
-                                                      const float* __restrict__ k,
+__global__ __launch_bounds__(kThreads) void pass2_f32(const float* __restrict__ q, Keys keys,
                                                       const float* __restrict__ c2,
                                                       float* __restrict__ scores, int64_t Nq,
                                                       int64_t N, int64_t S, int64_t m_chunk,
-                                                      int64_t nq, int64_t kv_stride, int64_t R,
-                                                      int64_t tiles, int32_t Hq, int32_t Hkv,
-                                                      float c1) {
+                                                      int64_t nq, int64_t R, int64_t tiles,
+                                                      int32_t Hq, int32_t Hkv, float c1) {
   const int64_t b = blockIdx.x;
   const int64_t tile = b % tiles;
   const int64_t r = (b / tiles) % R;
@@ -83,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void pass2_f32(const float* __restrict__ 
   }
   const int64_t key = c0 + tile * kThreads + threadIdx.x;
   if (key >= c1e) return;
-  const float* kr = k + ((l * Hkv + g) * kv_stride + key) * D;
+  const float* kr = key_row(keys, l * Hkv + g, key, D);
   float kv[D];
 #pragma unroll
   for (int t = 0; t < D; ++t) kv[t] = kr[t];
@@ -109,18 +119,18 @@ __global__ __launch_bounds__(kThreads) void pass2_f32(const float* __restrict__ 
 }
 
 template <int D>
-int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k, float* scores,
+int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const KvSrc& kv, float* scores,
         void* ws, hipStream_t st) {
   float* c2 = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_c2);
   const int64_t N = p.n_cache;
-  const int64_t stride = p.kv_row_stride ? p.kv_row_stride : N;
   const float c1 = (float)(1.4426950408889634 / sqrt((double)D));
   const float* qf = static_cast<const float*>(q);
-  const float* kf = static_cast<const float*>(k);
+  const Keys keys{static_cast<const float*>(kv.k_head), static_cast<const float*>(kv.k_tail),
+                  kv.head_stride, kv.tail_stride, kv.tail_row0, kv.split};
   {
   TraceScope t1("score_pass1_f32", st);
   hipLaunchKernelGGL(pass1_f32<D>, dim3((unsigned)ceil_div(pl.total_rows, kThreads)),
-                     dim3(kThreads), 0, st, qf, kf, c2, pl.total_rows, pl.n_queries, N, stride,
+                     dim3(kThreads), 0, st, qf, keys, c2, pl.total_rows, pl.n_queries, N,
                      p.q_heads, p.kv_heads, c1);
   }
   if (hipError_t e = hipGetLastError()) return (int)e;
@@ -128,9 +138,8 @@ int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
   {
   TraceScope t2("score_pass2_f32", st);
   hipLaunchKernelGGL(pass2_f32<D>, dim3((unsigned)(pl.units * pl.n_chunks * tiles)),
-                     dim3(kThreads), 0, st, qf, kf, c2, scores, pl.n_queries, N, p.n_sinks,
-                     p.chunk_size, p.q_per_chunk, stride, pl.n_chunks, tiles, p.q_heads,
-                     p.kv_heads, c1);
+                     dim3(kThreads), 0, st, qf, keys, c2, scores, pl.n_queries, N, p.n_sinks,
+                     p.chunk_size, p.q_per_chunk, pl.n_chunks, tiles, p.q_heads, p.kv_heads, c1);
   }
   if (hipError_t e = hipGetLastError()) return (int)e;
   return 0;
@@ -143,11 +152,11 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(float* dst, int64_t n, f
 
 }  // namespace
 
-int launch_score_f32(const kvs_problem& p, const ScorePlan& pl, const void* q, const void* k,
+int launch_score_f32(const kvs_problem& p, const ScorePlan& pl, const void* q, const KvSrc& kv,
                      float* scores, void* ws, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (p.head_dim == 128) return run<128>(p, pl, q, k, scores, ws, st);
-  return run<64>(p, pl, q, k, scores, ws, st);
+  if (p.head_dim == 128) return run<128>(p, pl, q, kv, scores, ws, st);
+  return run<64>(p, pl, q, kv, scores, ws, st);
 }
 
 int launch_fill(float* dst, int64_t n, float value, void* stream) {

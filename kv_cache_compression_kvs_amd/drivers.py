@@ -6,6 +6,8 @@ BlockLoop   EpiCache review ("[26'ICML] EpiCache"), "방법: 3단계" (2) and
             budget M, the episode prompt's queries score it and it is
             compressed back to M rows per (layer, KV head).  Two cache buffers
             of M + block rows alternate (ping-pong), so peak memory is fixed.
+            A block that triggers a compression is read in place rather than
+            copied behind the cache first.
 episodic    EpiCache review, "방법: 3단계" (2) and Fig. 3(b), with the
             "+α: 레이어별 예산 배분" budget split: one compressed cache per
             episode, built from that episode's prompt queries.
@@ -41,10 +43,10 @@ class BlockLoop:
         self.cur = 0
         self.n = 0
 
-    def problem(self, n: int) -> api.KvsProblem:
+    def problem(self, n: int, strided: bool = True) -> api.KvsProblem:
         chunk = max(n - self.S, 1)   # one chunk over every non-sink position
         return api.make_problem(self.L, self.Hq, self.Hkv, self.d, n, self.S, chunk, self.nq,
-                                self.dtype, kv_row_stride=self.cap)
+                                self.dtype, kv_row_stride=self.cap if strided else 0)
 
     def reset(self) -> None:
         self.cur = 0
@@ -52,11 +54,25 @@ class BlockLoop:
 
     def step(self, b: int, k_tokens: torch.Tensor, v_tokens: torch.Tensor,
              q_step: torch.Tensor) -> bool:
-        """Append block b; compress if the cache exceeds M.  Returns True if scored."""
+        """Append block b; compress if the cache exceeds M.  Returns True if scored.
+
+        A block that fills the cache past M is not copied in: the compression
+        reads the kept cache and the block where they lie (two segments) and
+        gathers the kept rows of both into the other buffer."""
         T = k_tokens.shape[2]
         r0 = b * self.B
         nb = min(self.B, T - r0)
         slabs = self.L * self.Hkv
+        nxt = 1 - self.cur
+        if self.n + nb > self.M and self.n % 8 == 0:
+            p = self.problem(self.n + nb, strided=False)
+            api.kvs_compress_block_seg(p, q_step, self.k[self.cur], self.v[self.cur], self.n,
+                                       self.cap, k_tokens, v_tokens, r0, T, self.M * self.L,
+                                       None, 0.0, self.scores, self.kept, self.k[nxt],
+                                       self.v[nxt], out_row_stride=self.cap, ws=self.ws)
+            self.cur = nxt
+            self.n = self.M
+            return True
         api.kvs_append_rows(slabs, self.d, self.dtype, k_tokens, T, r0, nb,
                             self.k[self.cur], self.cap, self.n)
         api.kvs_append_rows(slabs, self.d, self.dtype, v_tokens, T, r0, nb,
@@ -65,7 +81,6 @@ class BlockLoop:
         if self.n <= self.M:
             return False
         p = self.problem(self.n)
-        nxt = 1 - self.cur
         api.kvs_compress_block(p, q_step, self.k[self.cur], self.v[self.cur],
                                self.M * self.L, None, 0.0, self.scores, self.kept,
                                self.k[nxt], self.v[nxt], out_row_stride=self.cap, ws=self.ws)

@@ -210,3 +210,39 @@ def test_append_rejects_bad_ranges(K):
     assert h.kvs_append_rows(4, 128, 1, None, 100, 0, 20, FAKE, 200, 0, None) == 1
     assert h.kvs_append_rows(4, 128, 1, FAKE + 8, 100, 0, 20, FAKE, 200, 0, None) == 5
     assert h.kvs_append_rows(4, 128, 1, None, 100, 0, 0, None, 200, 0, None) == 0  # nothing to do
+
+
+def seg(K, k_head=None, v_head=None, head_rows=0, head_row_stride=0, k_tail=None, v_tail=None,
+        tail_row0=0, tail_row_stride=0):
+    return K.KvsKvSegments(k_head, v_head, head_rows, head_row_stride, k_tail, v_tail, tail_row0,
+                           tail_row_stride)
+
+
+def test_compress_block_seg_rejects_bad_segments(K):
+    h = raw(K)
+    p = prob(K)   # N = 4300
+    ws = K.kvs_workspace_bytes(p)
+    kl = (ctypes.c_int64 * 2)(-7, -7)
+
+    def call(sg, prob_=p, total=200):
+        return h.kvs_compress_block_seg(ctypes.byref(prob_), FAKE,
+                                        ctypes.byref(sg) if sg is not None else None, total,
+                                        None, 0.0, FAKE, FAKE, FAKE, FAKE, 0, kl, FAKE, ws, None)
+
+    good = dict(k_head=FAKE, v_head=FAKE, head_rows=4096, head_row_stride=6144, k_tail=FAKE,
+                v_tail=FAKE, tail_row0=2048, tail_row_stride=16384)
+    assert call(None) == 1
+    assert call(seg(K, **good), prob_=prob(K, kv_row_stride=4300)) == 2
+    for bad in (dict(head_rows=4093), dict(head_rows=4301), dict(head_rows=-8),
+                dict(head_row_stride=4088), dict(tail_row0=-1),
+                dict(tail_row0=16384 - 203), dict(tail_row_stride=2048 + 203)):
+        assert call(seg(K, **{**good, **bad})) == 2, bad
+    assert call(seg(K, **{**good, "k_tail": None})) == 1
+    assert call(seg(K, **{**good, "v_tail": None})) == 1
+    assert call(seg(K, **{**good, "k_head": None})) == 1
+    assert call(seg(K, **{**good, "v_tail": FAKE + 8})) == 5
+    # all rows in the head: the tail is never read, so it may be NULL; a NULL
+    # head is still an error
+    assert call(seg(K, **{**good, "head_rows": 4300, "k_head": None, "k_tail": None})) == 1
+    # an infeasible budget is still reported, and k_per_layer_out left alone
+    assert call(seg(K, **good), total=6) == 4 and list(kl) == [-7, -7]
