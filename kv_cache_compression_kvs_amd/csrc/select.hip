@@ -11,13 +11,16 @@
 //  2. MSB-first radix select in four 8-bit rounds finds the exact key tau of
 //     the (k - S)-th best candidate and e, the number of candidates equal to
 //     tau that must be kept (the lowest positions among the ties).
-//     Histograms live in LDS.  Scores cluster in a few exponents, so the top
-//     byte has few distinct values: the first round aggregates equal bins
-//     across a wave (ballot) before the LDS atomic.
+//     Histograms live in LDS, one per wave (no contention between waves),
+//     summed per bin before the digit is picked.  Each thread loads a batch
+//     of keys before counting any, so uncached passes keep many loads in
+//     flight instead of waiting on one at a time.
 //  3. One ordered sweep writes the output: a block-wide scan of packed
 //     (count above tau, count equal to tau) per thread gives each kept
 //     position its rank: S + above_before + min(equal_before, e).
 // Integer-only atomics on counts: the result does not depend on scheduling.
+#include <algorithm>
+
 #include "kvs_device.h"
 #include "kvs_internal.h"
 #include "kvs_trace.h"
@@ -27,8 +30,9 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kItems = 4;                 // consecutive candidates per thread in the sweep
-constexpr int64_t kLdsKeys = 36 * 1024;   // candidates cached in LDS (144 KiB)
+constexpr int kItems = 16;                // consecutive candidates per thread in the sweep
+constexpr int kBatch = 8;                 // candidates per thread per histogram iteration
+constexpr int64_t kLdsKeys = 32 * 1024;   // candidates cached in LDS (128 KiB)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t b = __float_as_uint(f);
@@ -70,32 +74,18 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint3
   return x;
 }
 
-__global__ __launch_bounds__(kThreads) void select_kernel(SelArgs a) {
-  __shared__ uint32_t keys[kLdsKeys];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[2 * kWaves];
-  __shared__ uint32_t pick[2];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int64_t unit = blockIdx.x;
-  const int64_t l = unit / a.Hkv, g = unit % a.Hkv;
-  const int64_t kl = a.t.k[l];
-  const int64_t N = a.N;
-  const int64_t S = a.S < N ? a.S : N;
-  const float* srow = a.scores + unit * N + S;
-  int32_t* out = a.kept + a.t.off[l] + g * kl;
-  const int64_t nc = N - S;
-  const int64_t need = kl - S;
-
-  for (int64_t i = tid; i < S; i += kThreads) out[i] = (int32_t)i;
-  if (need <= 0) return;  // only the sinks (uniform: no barrier skipped by part of the group)
-
-  const bool cached = nc <= kLdsKeys;
-  if (cached) {
-    for (int64_t i = tid; i < nc; i += kThreads) keys[i] = order_key(srow[i]);
-    __syncthreads();
-  }
-  auto key_at = [&](int64_t i) -> uint32_t { return cached ? keys[i] : order_key(srow[i]); };
+// Radix select and ordered sweep over the nc candidates of one (layer, KV
+// head), keys read from the LDS cache (CACHED) or from global memory.  The
+// choice is made once per workgroup so that no key load sits behind a
+// per-element branch: every load is unconditional, from a clamped position.
+template <bool CACHED>
+__device__ __forceinline__ void select_body(const float* srow, const uint32_t* keys, uint32_t* hw,
+                                            uint32_t* wsum, uint32_t* pick, int32_t* out,
+                                            int64_t nc, int64_t need, int64_t S, int64_t kl) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  auto key_at = [&](int64_t i) __attribute__((always_inline)) -> uint32_t {
+    return CACHED ? keys[i] : order_key(srow[i]);
+  };
 
   uint32_t tau = 0u;
   uint32_t e = 0u;
@@ -106,34 +96,43 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelArgs a) {
     uint32_t prefix = 0u, mask = 0u;
     uint32_t rem = (uint32_t)need;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0u;
+      for (int b = tid; b < kWaves * 256; b += kThreads) hw[b] = 0u;
       __syncthreads();
-      for (int64_t base = 0; base < nc; base += kThreads) {
-        const int64_t i = base + tid;
-        bool active = false;
-        uint32_t bin = 0u;
-        if (i < nc) {
-          const uint32_t x = key_at(i);
-          active = (x & mask) == prefix;
-          bin = (x >> shift) & 255u;
-        }
-        // Aggregate lanes that share a bin: all distinct bins in round one,
-        // one pass (the most common case of a uniform wave) afterwards.
-        const int passes = (shift == 24) ? 64 : 1;
-        for (int it = 0; it < passes; ++it) {
+      // One histogram per wave, so waves never contend; lanes of a wave that
+      // hit the same bin are serialised by the LDS atomic unit.  kBatch
+      // candidates per thread (coalesced, kThreads apart) are loaded before
+      // any is counted, so that many loads are in flight when the keys come
+      // from global memory.
+      uint32_t* mine = hw + wave * 256;
+      for (int64_t base = 0; base < nc; base += (int64_t)kThreads * kBatch) {
+        uint32_t xs[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) xs[j] = key_at(min(base + (int64_t)j * kThreads + tid, nc - 1));
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int64_t i = base + (int64_t)j * kThreads + tid;
+          bool active = i < nc && (xs[j] & mask) == prefix;
+          const uint32_t bin = (xs[j] >> shift) & 255u;
+          // Scores cluster, so most active lanes usually share one bin: count
+          // the first active lane's bin for the whole wave with one atomic,
+          // then the remaining lanes individually.
           const uint64_t act = __ballot(active);
-          if (act == 0ull) break;
-          const int leader = __ffsll((unsigned long long)act) - 1;
-          const uint32_t lb = __shfl(bin, leader, 64);
-          const uint64_t same = __ballot(active && bin == lb);
-          if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
-          if (active && bin == lb) active = false;
+          if (act != 0ull) {
+            const int leader = __ffsll((unsigned long long)act) - 1;
+            const uint32_t lb = __shfl(bin, leader, 64);
+            const uint64_t same = __ballot(active && bin == lb);
+            if (lane == leader) atomicAdd(&mine[lb], (uint32_t)__popcll(same));
+            if (active && bin != lb) atomicAdd(&mine[bin], 1u);
+          }
         }
-        if (active) atomicAdd(&hist[bin], 1u);
       }
       __syncthreads();
       // counts from the top bin down; the digit is where the running count reaches rem
-      const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
+      uint32_t c = 0u;
+      if (tid < 256) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) c += hw[w * 256 + 255 - tid];
+      }
       uint32_t tot;
       const uint32_t cum = block_scan(c, wsum, &tot);
       if (tid < 256 && cum >= rem && cum - c < rem) {
@@ -150,18 +149,17 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelArgs a) {
     e = rem;
   }
 
-  // ordered sweep
+  // ordered sweep: kItems consecutive candidates per thread
   uint64_t run_gt = 0, run_eq = 0;
   for (int64_t base = 0; base < nc; base += (int64_t)kThreads * kItems) {
     const int64_t i0 = base + (int64_t)tid * kItems;
     uint32_t x[kItems];
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) x[j] = key_at(min(i0 + j, nc - 1));
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
-      const int64_t i = i0 + j;
-      x[j] = 0u;
-      if (i < nc) {
-        x[j] = key_at(i);
+      if (i0 + j < nc) {
         ngt += x[j] > tau;
         neq += x[j] == tau;
       }
@@ -175,14 +173,13 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelArgs a) {
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
       const int64_t i = i0 + j;
-      if (i >= nc) break;
       // positions are < k by construction; the bound check only keeps a
       // counting error from ever writing outside this list
-      if (x[j] > tau) {
+      if (i < nc && x[j] > tau) {
         const uint64_t pos = (uint64_t)S + gt_before + (eq_before < e ? eq_before : e);
         if (pos < (uint64_t)kl) out[pos] = (int32_t)(S + i);
         ++gt_before;
-      } else if (x[j] == tau) {
+      } else if (i < nc && x[j] == tau) {
         const uint64_t pos = (uint64_t)S + gt_before + eq_before;
         if (eq_before < e && pos < (uint64_t)kl) out[pos] = (int32_t)(S + i);
         ++eq_before;
@@ -191,6 +188,38 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelArgs a) {
     run_gt += tot >> 16;
     run_eq += tot & 0xFFFFu;
   }
+}
+
+// One workgroup per (layer, KV head).  CACHED: the candidates fit the LDS key
+// cache.  Otherwise the keys are read from global memory in every pass and
+// the kernel needs only the histograms' 16 KiB of LDS, so two workgroups fit
+// on a CU.
+template <bool CACHED>
+__global__ __launch_bounds__(kThreads) void select_kernel(SelArgs a) {
+  __shared__ uint32_t keys[CACHED ? kLdsKeys : 1];
+  __shared__ uint32_t hw[kWaves * 256];
+  __shared__ uint32_t wsum[2 * kWaves];
+  __shared__ uint32_t pick[2];
+
+  const int tid = threadIdx.x;
+  const int64_t unit = blockIdx.x;
+  const int64_t l = unit / a.Hkv, g = unit % a.Hkv;
+  const int64_t kl = a.t.k[l];
+  const int64_t N = a.N;
+  const int64_t S = a.S < N ? a.S : N;
+  const float* srow = a.scores + unit * N + S;
+  int32_t* out = a.kept + a.t.off[l] + g * kl;
+  const int64_t nc = N - S;
+  const int64_t need = kl - S;
+
+  for (int64_t i = tid; i < S; i += kThreads) out[i] = (int32_t)i;
+  if (need <= 0) return;  // only the sinks (uniform: no barrier skipped by part of the group)
+
+  if (CACHED) {
+    for (int64_t i = tid; i < nc; i += kThreads) keys[i] = order_key(srow[i]);
+    __syncthreads();
+  }
+  select_body<CACHED>(srow, keys, hw, wsum, pick, out, nc, need, S, kl);
 }
 
 }  // namespace
@@ -206,9 +235,14 @@ int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t
   a.S = p.n_sinks;
   a.Hkv = p.kv_heads;
   a.t = t;
+  const int64_t nc = p.n_cache - std::min(p.n_sinks, p.n_cache);
   TraceScope ts("select", static_cast<hipStream_t>(stream));
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)units), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
+  if (nc <= kLdsKeys)
+    hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)units), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL(select_kernel<false>, dim3((unsigned)units), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
 

@@ -127,6 +127,9 @@ SEL = [
     (2, 1, 6144, 4, "coarse", [4096]),
     (1, 1, 32768, 4, "uniform", [1638]),        # LDS-resident path, largest size
     (1, 1, 40000, 4, "coarse", [2000]),          # global-memory path
+    (1, 1, 32772, 4, "uniform", [1000]),         # exactly fills the LDS cache
+    (1, 1, 32773, 4, "uniform", [1000]),         # one candidate too many: global path
+    (2, 1, 100003, 4, "sparse", [5000]),         # global path, ragged batches
     (1, 1, 131072, 4, "uniform", [2621]),
     (1, 1, 131072, 4, "equal", [2621]),
     (2, 1, 700, 4, "uniform", [700]),            # keep everything
