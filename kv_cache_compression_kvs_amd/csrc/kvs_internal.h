@@ -73,5 +73,6 @@ constexpr int kP2Waves = 4;       // pass-2 waves per workgroup, 64 keys each
 constexpr int kP2Keys = kP2Waves * 64;  // keys per pass-2 workgroup
 constexpr int kP2Ring = 3;        // pass-2 LDS query tiles in flight
 constexpr int kMaxSplits = 64;
+constexpr int kP1Slots = 512;     // resident pass-1 workgroups: 2 per CU x 256 CUs
 
 }  // namespace kvs
