@@ -37,6 +37,15 @@ What it computes, step by step, with the passage each step follows:
               budget after every block, which bounds peak memory.
   episodes    EpiCache review, "방법: 3단계" (2) and Fig. 3(b): one compressed
               cache is built per episode from that episode's prompt queries.
+  queries     KV² summary, "어떻게 동작하나" (stage 1, query selection): the
+              per-(layer, KV head) scores of a token are averaged into one
+              token score p_i (the page found the mean better than the max),
+              and each chunk takes its n_q = max(floor(rho |C_r|), 1)
+              best-scoring positions as its reconstruction queries; they need
+              not be contiguous.  Section "무엇과 다른가": stage 2's scores
+              have the same token granularity and can replace the stage-1
+              proxy for another pass (refinement); this is that selection.
+              Ties go to the lower position; each chunk's list is ascending.
 
 Every pin of these functions lives in tests/test_oracle_*.py.
 """
@@ -309,3 +318,50 @@ def episodic(k, v, q_episodes, sens, alpha: float, total: int, n_sinks: int,
     kl = layer_budgets(total, L, sens, alpha, n_cache=N, n_sinks=n_sinks)
     return kl, [compress(q_episodes[e], k, v, n_sinks, chunk_size, q_per_chunk, kl)
                 for e in range(q_episodes.shape[0])]
+
+
+# ---------------------------------------------------------------------------
+# stage-1 query selection (KV² summary, "어떻게 동작하나"; the refinement pass
+# of "무엇과 다른가" feeds it stage-2 scores)
+# ---------------------------------------------------------------------------
+
+def query_counts(n_cache: int, n_sinks: int, chunk_size: int, rho: float) -> List[int]:
+    """n_q of every chunk: max(floor(rho * |C_r|), 1), the product in IEEE double."""
+    if not (0.0 < rho <= 1.0):
+        raise ValueError("rho must lie in (0, 1]")
+    return [max(int(math.floor(rho * (b - a))), 1)
+            for a, b in chunk_bounds(n_cache, n_sinks, chunk_size)]
+
+
+def token_scores(score: np.ndarray) -> np.ndarray:
+    """p_i: the mean over layers and KV heads of score[l, g, i]  ([L, Hkv, N] -> [N])."""
+    s = np.asarray(score, np.float64)
+    return s.reshape(-1, s.shape[-1]).mean(axis=0)
+
+
+def token_sums_f32(score: np.ndarray) -> np.ndarray:
+    """The GPU's ranking key for p: the float32 sum over (l, g), layer-major, one
+    unit at a time.  Dividing by L * Hkv would not change the order, so the
+    sum is ranked directly; both sides must round the same way because the
+    ranking decides which positions are chosen."""
+    s = np.asarray(score, np.float32)
+    s = s.reshape(-1, s.shape[-1])
+    acc = np.zeros(s.shape[1], np.float32)
+    for u in range(s.shape[0]):
+        acc = np.add(acc, s[u], dtype=np.float32)
+    return acc
+
+
+def select_queries(p: np.ndarray, n_cache: int, n_sinks: int, chunk_size: int,
+                   rho: float) -> List[np.ndarray]:
+    """Per chunk, ascending: the n_q positions of C_r with the largest p, ties to
+    the lower position."""
+    p = np.asarray(p)
+    out = []
+    for (a, b), nq in zip(chunk_bounds(n_cache, n_sinks, chunk_size),
+                          query_counts(n_cache, n_sinks, chunk_size, rho)):
+        cand = np.arange(a, b)
+        order = np.lexsort((cand, -p[a:b].astype(np.float64)))
+        out.append(np.sort(cand[order[:nq]]).astype(np.int64))
+    return out
+
