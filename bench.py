@@ -221,6 +221,37 @@ def main():
         "input_generation_s": round(t_gen, 2),
     }
 
+    # ---- stage-1 query selection on the final scores (KV² refinement pass) -------
+    # Outside the timed step: the chunked workloads' stage-2 scores choose the
+    # next pass's reconstruction queries (rho = 10%, as in their configs).
+    if w.kind != "block_loop" and s.n_chunks > 1 and not args.no_trace:
+        rho = 0.1
+        qcounts = K.kvs_query_counts(p, rho)
+        qtotal = int(qcounts.sum())
+        qpos = torch.empty(qtotal, dtype=torch.int32, device=dev)
+        qws = torch.empty(max(K.kvs_query_workspace_bytes(p), 256), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            K.kvs_query_select(p, scores, rho, qpos, qws)
+        torch.cuda.synchronize()
+        K.kvs_trace_summary()
+        K.kvs_trace_only(None)
+        K.kvs_trace_enable(True)
+        reps = 10
+        for _ in range(reps):
+            K.kvs_query_select(p, scores, rho, qpos, qws)
+        torch.cuda.synchronize()
+        K.kvs_trace_enable(False)
+        qtr = K.kvs_trace_summary()
+        q_ms = sum(v["total_ms"] for v in qtr.values()) / reps
+        nc = s.n_cache - min(s.n_sinks, s.n_cache)
+        q_bytes = 4 * L * Hkv * s.n_cache + 2 * 4 * nc + 4 * qtotal
+        rec["next_rows"] = {"f1_query_select": {
+            "rho": rho, "queries": qtotal, "ms_per_call": round(q_ms, 5),
+            "algorithmic_bytes": q_bytes,
+            "GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "kernels": {k: round(v["avg_ms"], 5) for k, v in qtr.items()}}}
+
     # ---- float64 oracle on a bounded sample of the same workload ---------------
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, kl)

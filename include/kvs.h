@@ -223,6 +223,34 @@ int kvs_compress_block_seg(const kvs_problem* p, const void* q, const kvs_kv_seg
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Stage-1 query selection (KV² summary, "어떻게 동작하나"), also the selection
+ * half of the refinement pass of "무엇과 다른가" when `scores` are stage-2
+ * scores.  The token score of position i is the mean over layers and KV heads
+ * of scores[l, g, i]; it is ranked by the float32 sum over the L * Hkv units in
+ * layer-major order (same order as the mean, up to rounding).  Each chunk r of
+ * p (positions [S + r*m, min(S + (r+1)*m, N))) keeps its
+ *     n_q(r) = max(floor(rho * |C_r|), 1)
+ * best positions (the product in IEEE double), ties to the lower position.
+ *
+ * kvs_query_counts (host only): n_q(r) for r < R into counts[R] and their sum
+ *   into *total (either may be NULL).
+ * kvs_query_select: scores device [L, Hkv, N] fp32 (e.g. kvs_score's output;
+ *   q_heads, head_dim and q_per_chunk of p are not used but must be valid).
+ *   positions: device int32, chunk after chunk, each chunk's n_q(r) positions
+ *   ascending; chunk r starts at r * n_q of a full chunk, so the list has the
+ *   total of kvs_query_counts entries.  ws: device workspace of at least
+ *   kvs_query_workspace_bytes(p) bytes (the token sums).
+ * Errors: KVS_E_SHAPE as kvs_check_problem; KVS_E_BUDGET for rho outside
+ * (0, 1] or NaN; KVS_E_NULL, KVS_E_ALIGN (scores, positions 4-byte, ws
+ * 256-byte aligned), KVS_E_WORKSPACE.  With no chunk (N <= S) nothing is
+ * written.
+ */
+size_t kvs_query_workspace_bytes(const kvs_problem* p);
+int kvs_query_counts(const kvs_problem* p, double rho, int64_t* counts, int64_t* total);
+int kvs_query_select(const kvs_problem* p, const float* scores, double rho, int32_t* positions,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Block append for the block-prefill loop (EpiCache review, "방법: 3단계" (2),
  * Fig. 1(b)): for each of `slabs` (layer, KV head) slabs copies rows
  * [src_row0, src_row0 + n_rows) of src (slab stride src_row_stride rows) to

@@ -7,6 +7,7 @@ from ._lib import (KVS_BF16, KVS_F32, KvsKvSegments, KvsLibraryMissing,  # noqa:
                    KvsProblem, LIB_PATH)
 from .api import (KvsError, kvs_append_rows, kvs_check_problem, kvs_compact,  # noqa: F401
                   kvs_compress_block, kvs_compress_block_seg, kvs_layer_budgets,
-                  kvs_num_chunks, kvs_num_queries, kvs_score, kvs_select, kvs_status_string,
+                  kvs_num_chunks, kvs_num_queries, kvs_query_counts, kvs_query_select,
+                  kvs_query_workspace_bytes, kvs_score, kvs_select, kvs_status_string,
                   kvs_trace_enable, kvs_trace_only, kvs_trace_summary, kvs_version,
                   kvs_workspace_bytes, make_problem, workspace)

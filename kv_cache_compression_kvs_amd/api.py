@@ -179,6 +179,32 @@ def kvs_compress_block_seg(p: KvsProblem, q: Tensorish, k_head: Tensorish, v_hea
     return np.array(kl[:], dtype=np.int64)
 
 
+def kvs_query_workspace_bytes(p: KvsProblem) -> int:
+    return int(_lib.lib().kvs_query_workspace_bytes(ctypes.byref(p)))
+
+
+def kvs_query_counts(p: KvsProblem, rho: float) -> np.ndarray:
+    """n_q of every chunk (host only)."""
+    R = kvs_num_chunks(p)
+    counts = (ctypes.c_int64 * max(R, 1))()
+    total = ctypes.c_int64(0)
+    _check(_lib.lib().kvs_query_counts(ctypes.byref(p), float(rho), counts, ctypes.byref(total)),
+           "kvs_query_counts")
+    return np.array(counts[:R], dtype=np.int64)
+
+
+def kvs_query_select(p: KvsProblem, scores: Tensorish, rho: float, positions: Tensorish,
+                     ws: Tensorish = None, ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws is None:
+        ws = torch.empty(max(kvs_query_workspace_bytes(p), 256), dtype=torch.uint8,
+                         device=scores.device)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    _check(_lib.lib().kvs_query_select(ctypes.byref(p), _dev(scores, "scores"), float(rho),
+                                       _dev(positions, "positions"), _dev(ws, "ws"), ws_bytes,
+                                       _stream(stream)), "kvs_query_select")
+
+
 def kvs_append_rows(slabs: int, head_dim: int, dtype: Union[int, torch.dtype], src: Tensorish,
                     src_row_stride: int, src_row0: int, n_rows: int, dst: Tensorish,
                     dst_row_stride: int, dst_row0: int, stream=None) -> None:

@@ -392,6 +392,43 @@ int kvs_compress_block_seg(const kvs_problem* p, const void* q, const kvs_kv_seg
                   out_row_stride, k_per_layer_out, ws, ws_bytes, stream);
 }
 
+size_t kvs_query_workspace_bytes(const kvs_problem* p) {
+  if (check(p) != KVS_OK) return 0;
+  const int64_t nc = p->n_cache - std::min(p->n_sinks, p->n_cache);
+  return round256(sizeof(float) * (size_t)nc);
+}
+
+int kvs_query_counts(const kvs_problem* p, double rho, int64_t* counts, int64_t* total) {
+  int st = check(p);
+  if (st) return st;
+  if (!(rho > 0.0 && rho <= 1.0)) return KVS_E_BUDGET;
+  const int64_t R = chunks_of(*p);
+  const int64_t S = std::min(p->n_sinks, p->n_cache);
+  int64_t sum = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t len = std::min(p->chunk_size, p->n_cache - (S + r * p->chunk_size));
+    const int64_t nq = std::max<int64_t>((int64_t)std::floor(rho * (double)len), 1);
+    if (counts) counts[r] = nq;
+    sum += nq;
+  }
+  if (total) *total = sum;
+  return KVS_OK;
+}
+
+int kvs_query_select(const kvs_problem* p, const float* scores, double rho, int32_t* positions,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  if (!(rho > 0.0 && rho <= 1.0)) return KVS_E_BUDGET;
+  if (chunks_of(*p) == 0) return KVS_OK;  // every position is a sink: no queries
+  const size_t need = kvs_query_workspace_bytes(p);
+  if (!scores || !positions || !ws) return KVS_E_NULL;
+  if (ws_bytes < need) return KVS_E_WORKSPACE;
+  if (!aligned(scores, 4) || !aligned(positions, 4) || !aligned(ws, 256)) return KVS_E_ALIGN;
+  if ((int64_t)p->layers * p->kv_heads * p->n_cache >= (int64_t(1) << 40)) return KVS_E_SHAPE;
+  return to_status(launch_query_select(*p, scores, rho, positions, static_cast<float*>(ws), stream));
+}
+
 int kvs_append_rows(int32_t slabs, int32_t head_dim, int32_t dtype, const void* src,
                     int64_t src_row_stride, int64_t src_row0, int64_t n_rows, void* dst,
                     int64_t dst_row_stride, int64_t dst_row0, void* stream) {

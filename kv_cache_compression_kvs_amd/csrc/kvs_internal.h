@@ -58,6 +58,8 @@ int launch_score_f32(const kvs_problem& p, const ScorePlan& pl, const void* q,
 int launch_fill(float* dst, int64_t n, float value, void* stream);
 int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t,
                   int32_t* kept, void* stream);
+int launch_query_select(const kvs_problem& p, const float* scores, double rho, int32_t* out,
+                        float* psum, void* stream);
 int launch_compact(const kvs_problem& p, const KvSrc& kv, const int32_t* kept,
                    const LayerTable& t, int32_t k_max, void* k_out, void* v_out,
                    int64_t out_row_stride, void* stream);

@@ -78,10 +78,13 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint3
 // head), keys read from the LDS cache (CACHED) or from global memory.  The
 // choice is made once per workgroup so that no key load sits behind a
 // per-element branch: every load is unconditional, from a clamped position.
+//
+// Writes the ranks 0 .. need-1 of out: the chosen candidates' positions val0 + i,
+// ascending.
 template <bool CACHED>
 __device__ __forceinline__ void select_body(const float* srow, const uint32_t* keys, uint32_t* hw,
                                             uint32_t* wsum, uint32_t* pick, int32_t* out,
-                                            int64_t nc, int64_t need, int64_t S, int64_t kl) {
+                                            int64_t nc, int64_t need, int64_t val0) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   auto key_at = [&](int64_t i) __attribute__((always_inline)) -> uint32_t {
     return CACHED ? keys[i] : order_key(srow[i]);
@@ -173,15 +176,15 @@ __device__ __forceinline__ void select_body(const float* srow, const uint32_t* k
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
       const int64_t i = i0 + j;
-      // positions are < k by construction; the bound check only keeps a
+      // ranks are < need by construction; the bound check only keeps a
       // counting error from ever writing outside this list
       if (i < nc && x[j] > tau) {
-        const uint64_t pos = (uint64_t)S + gt_before + (eq_before < e ? eq_before : e);
-        if (pos < (uint64_t)kl) out[pos] = (int32_t)(S + i);
+        const uint64_t rank = gt_before + (eq_before < e ? eq_before : e);
+        if (rank < (uint64_t)need) out[rank] = (int32_t)(val0 + i);
         ++gt_before;
       } else if (i < nc && x[j] == tau) {
-        const uint64_t pos = (uint64_t)S + gt_before + eq_before;
-        if (eq_before < e && pos < (uint64_t)kl) out[pos] = (int32_t)(S + i);
+        const uint64_t rank = gt_before + eq_before;
+        if (eq_before < e && rank < (uint64_t)need) out[rank] = (int32_t)(val0 + i);
         ++eq_before;
       }
     }
@@ -219,7 +222,68 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelArgs a) {
     for (int64_t i = tid; i < nc; i += kThreads) keys[i] = order_key(srow[i]);
     __syncthreads();
   }
-  select_body<CACHED>(srow, keys, hw, wsum, pick, out, nc, need, S, kl);
+  select_body<CACHED>(srow, keys, hw, wsum, pick, out + S, nc, need, S);
+}
+
+// Stage-1 query selection (KV² summary, "어떻게 동작하나"): token score =
+// mean over layers and KV heads of the per-head scores, ranked by the float32
+// sum over the units in layer-major order (the same order as the mean, up to
+// rounding, with a rounding both sides can reproduce).  One thread per
+// position; a batch of units is loaded before any is added.
+constexpr int kSumThreads = 256;
+constexpr int kSumBatch = 8;
+
+__global__ __launch_bounds__(kSumThreads) void unit_sum_kernel(const float* __restrict__ scores,
+                                                               float* __restrict__ psum, int64_t N,
+                                                               int64_t S, int64_t units) {
+  const int64_t i = S + (int64_t)blockIdx.x * kSumThreads + threadIdx.x;
+  if (i >= N) return;
+  const float* col = scores + i;
+  float acc = 0.f;
+  int64_t u = 0;
+  for (; u + kSumBatch <= units; u += kSumBatch) {
+    float v[kSumBatch];
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j) v[j] = col[(u + j) * N];
+#pragma unroll
+    for (int j = 0; j < kSumBatch; ++j) acc += v[j];
+  }
+  for (; u < units; ++u) acc += col[u * N];
+  psum[i - S] = acc;
+}
+
+// Per chunk r: the n_q = max(floor(rho |C_r|), 1) positions with the largest
+// token score (ties to the lower position), ascending, at offset r * n_q of a
+// full chunk.  One workgroup per chunk.
+struct QueryArgs {
+  const float* psum;   // token sums of positions [S, N)
+  int32_t* out;
+  int64_t N, S, m;
+  double rho;
+};
+
+__device__ __forceinline__ int64_t n_queries_of(double rho, int64_t len) {
+  const int64_t n = (int64_t)floor(rho * (double)len);
+  return n > 1 ? n : 1;
+}
+
+template <bool CACHED>
+__global__ __launch_bounds__(kThreads) void query_select_kernel(QueryArgs a) {
+  __shared__ uint32_t keys[CACHED ? kLdsKeys : 1];
+  __shared__ uint32_t hw[kWaves * 256];
+  __shared__ uint32_t wsum[2 * kWaves];
+  __shared__ uint32_t pick[2];
+  const int64_t r = blockIdx.x;
+  const int64_t c0 = a.S + r * a.m;
+  const int64_t len = min(a.m, a.N - c0);
+  const int64_t nq = n_queries_of(a.rho, len);
+  const float* srow = a.psum + (c0 - a.S);
+  int32_t* out = a.out + r * n_queries_of(a.rho, a.m);
+  if (CACHED) {
+    for (int64_t i = threadIdx.x; i < len; i += kThreads) keys[i] = order_key(srow[i]);
+    __syncthreads();
+  }
+  select_body<CACHED>(srow, keys, hw, wsum, pick, out, len, nq, c0);
 }
 
 }  // namespace
@@ -243,6 +307,34 @@ int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t
   else
     hipLaunchKernelGGL(select_kernel<false>, dim3((unsigned)units), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), a);
+  return (int)hipGetLastError();
+}
+
+int launch_query_select(const kvs_problem& p, const float* scores, double rho, int32_t* out,
+                        float* psum, void* stream) {
+  const int64_t N = p.n_cache, S = std::min(p.n_sinks, p.n_cache);
+  if (N <= S) return 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t units = (int64_t)p.layers * p.kv_heads;
+  {
+    TraceScope ts("query_token_sum", st);
+    hipLaunchKernelGGL(unit_sum_kernel, dim3((unsigned)ceil_div(N - S, kSumThreads)),
+                       dim3(kSumThreads), 0, st, scores, psum, N, S, units);
+  }
+  if (hipError_t e = hipGetLastError()) return (int)e;
+  QueryArgs a;
+  a.psum = psum;
+  a.out = out;
+  a.N = N;
+  a.S = S;
+  a.m = p.chunk_size;
+  a.rho = rho;
+  const int64_t R = ceil_div(N - S, p.chunk_size);
+  TraceScope ts("query_select", st);
+  if (std::min(p.chunk_size, N - S) <= kLdsKeys)
+    hipLaunchKernelGGL(query_select_kernel<true>, dim3((unsigned)R), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(query_select_kernel<false>, dim3((unsigned)R), dim3(kThreads), 0, st, a);
   return (int)hipGetLastError();
 }
 

@@ -246,3 +246,37 @@ def test_compress_block_seg_rejects_bad_segments(K):
     assert call(seg(K, **{**good, "head_rows": 4300, "k_head": None, "k_tail": None})) == 1
     # an infeasible budget is still reported, and k_per_layer_out left alone
     assert call(seg(K, **good), total=6) == 4 and list(kl) == [-7, -7]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_query_counts_match_oracle(K, seed):
+    rng = np.random.default_rng(100 + seed)
+    N = int(rng.integers(1, 20000))
+    S = int(rng.integers(0, 8))
+    m = int(rng.integers(1, 5000))
+    rho = float(rng.choice([0.02, 0.1, 0.29, 0.5, 1.0]))
+    p = prob(K, n_cache=N, n_sinks=S, chunk_size=m, q_per_chunk=3)
+    got = K.kvs_query_counts(p, rho)
+    assert got.tolist() == O.query_counts(N, S, m, rho)
+    want_ws = 4 * max(N - min(S, N), 0)
+    assert K.kvs_query_workspace_bytes(p) >= want_ws and K.kvs_query_workspace_bytes(p) % 256 == 0
+
+
+def test_query_select_rejects_bad_arguments(K):
+    h = raw(K)
+    p = prob(K)
+    ws = K.kvs_query_workspace_bytes(p)
+    for rho in (0.0, -1.0, 1.0001, float("nan"), float("inf")):
+        assert h.kvs_query_select(ctypes.byref(p), FAKE, rho, FAKE, FAKE, ws, None) == 4, rho
+        assert h.kvs_query_counts(ctypes.byref(p), rho, None, None) == 4
+    assert h.kvs_query_select(ctypes.byref(p), None, 0.1, FAKE, FAKE, ws, None) == 1
+    assert h.kvs_query_select(ctypes.byref(p), FAKE, 0.1, None, FAKE, ws, None) == 1
+    assert h.kvs_query_select(ctypes.byref(p), FAKE, 0.1, FAKE, None, ws, None) == 1
+    assert h.kvs_query_select(ctypes.byref(p), FAKE, 0.1, FAKE, FAKE, ws - 1, None) == 6
+    assert h.kvs_query_select(ctypes.byref(p), FAKE + 2, 0.1, FAKE, FAKE, ws, None) == 5
+    assert h.kvs_query_select(ctypes.byref(p), FAKE, 0.1, FAKE, FAKE + 16, ws, None) == 5
+    bad = prob(K, head_dim=80)
+    assert h.kvs_query_select(ctypes.byref(bad), FAKE, 0.1, FAKE, FAKE, ws, None) == 2
+    # every position a sink: nothing to select, nothing touched
+    allsink = prob(K, n_cache=4)
+    assert h.kvs_query_select(ctypes.byref(allsink), None, 0.1, None, None, 0, None) == 0

@@ -122,6 +122,17 @@ def test_kv2_full(K, name):
         assert_kept_match(layers[l][g].cpu().numpy(), o, keep, s.n_sinks, f"{name} unit ({l},{g})")
     check_selection_all(scores, layers, s.n_sinks, name)
     check_compaction(x["k"], x["v"], layers, ko, vo, name)
+    # refinement: these stage-2 scores choose the next pass's queries
+    p = K.make_problem(s.layers, s.q_heads, s.kv_heads, s.head_dim, s.n_cache, s.n_sinks,
+                       s.chunk_size, s.q_per_chunk, x["k"].dtype)
+    counts = K.kvs_query_counts(p, 0.1)
+    pos = torch.full((int(counts.sum()),), -1, dtype=torch.int32, device="cuda")
+    K.kvs_query_select(p, scores.reshape(-1), 0.1, pos)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    want = np.concatenate(O.select_queries(O.token_sums_f32(sc), s.n_cache, s.n_sinks,
+                                           s.chunk_size, 0.1))
+    assert np.array_equal(pos.cpu().numpy().astype(np.int64), want), f"{name}: query selection"
     if name == "kv2_131k":  # planted needles: a sanity signal, most should survive at 2%
         needles = gen.needle_positions(s.n_cache, s.n_sinks).cuda()
         kept0 = layers[0][0].long()

@@ -1,0 +1,92 @@
+"""GPU stage-1 query selection against the oracle.
+
+The GPU ranks positions by the float32 layer-major sum of the per-unit scores,
+the same key the oracle's token_sums_f32 gives, so the positions must match
+exactly.  Against the float64 mean (the plain reading of the pages) the sets
+may differ only at positions whose mean lies within the float32 rounding of
+the sum (L * Hkv * 2^-24 relative) of the chunk's cut-off."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import kv_cache_compression_kvs_amd as pkg
+    return pkg
+
+
+def run_query_select(K, scores, L, Hkv, N, S, m, rho):
+    p = K.make_problem(L, Hkv, Hkv, 128, N, S, m, 1, torch.bfloat16)
+    counts = K.kvs_query_counts(p, rho)
+    total = int(counts.sum())
+    out = torch.full((max(total, 1),), -9, dtype=torch.int32, device="cuda")
+    K.kvs_query_select(p, scores.reshape(-1).cuda(), rho, out)
+    torch.cuda.synchronize()
+    got, off = [], 0
+    for c in counts:
+        got.append(out[off:off + int(c)].cpu().numpy().astype(np.int64))
+        off += int(c)
+    return got, counts
+
+
+def check_against_f64(got, s64, N, S, m, rho, U):
+    mean = O.token_scores(s64)
+    want = O.select_queries(mean, N, S, m, rho)
+    for (a, b), x, y in zip(O.chunk_bounds(N, S, m), got, want):
+        diff = set(x.tolist()) ^ set(y.tolist())
+        if not diff:
+            continue
+        cut = np.sort(mean[a:b])[::-1][len(y) - 1]
+        band = U * 2.0 ** -24 * max(abs(cut), np.abs(mean[a:b]).max()) * 2
+        for i in diff:
+            assert abs(mean[i] - cut) <= band, (i, mean[i], cut)
+
+
+CASES = [
+    # (L, Hkv, N, S, m, rho, kind)
+    (2, 2, 300, 4, 100, 0.1, "uniform"),
+    (2, 2, 300, 4, 100, 0.3, "coarse"),          # heavy ties
+    (3, 2, 1000, 0, 128, 0.05, "sparse"),
+    (4, 8, 32768, 4, 4096, 0.1, "uniform"),      # the KV² 32K shape
+    (1, 3, 40000, 4, 36000, 0.02, "uniform"),    # a chunk beyond the LDS cache
+    (2, 2, 5000, 4, 4096, 1.0, "coarse"),        # rho = 1: every position
+    (2, 2, 4103, 4, 4096, 0.1, "tiny"),          # last chunk of 3: one query
+    (1, 1, 4, 4, 100, 0.5, "uniform"),           # all sinks: no chunk
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_query_select_matches_oracle(K, case):
+    L, Hkv, N, S, m, rho, kind = case
+    scores = gen.score_tensor(L * Hkv, N, S, kind, seed=N + L).reshape(L, Hkv, N)
+    got, counts = run_query_select(K, scores, L, Hkv, N, S, m, rho)
+    assert counts.tolist() == O.query_counts(N, S, m, rho)
+    want = O.select_queries(O.token_sums_f32(scores.numpy()), N, S, m, rho)
+    assert len(got) == len(want)
+    for r, (x, y) in enumerate(zip(got, want)):
+        assert np.array_equal(x, y), f"chunk {r}"
+    check_against_f64(got, scores.double().numpy(), N, S, m, rho, L * Hkv)
+
+
+def test_refinement_on_stage_two_scores(K):
+    """Stage-2 scores from kvs_score drive the next selection (the refinement
+    pass's selection half)."""
+    from workloads import SMALL
+    w = SMALL["kv2_32k"]
+    s = w.shape
+    x = gen.single_inputs(w, device="cuda")
+    p = K.make_problem(s.layers, s.q_heads, s.kv_heads, s.head_dim, s.n_cache, s.n_sinks,
+                       s.chunk_size, s.q_per_chunk, x["k"].dtype)
+    scores = torch.empty(s.layers * s.kv_heads * s.n_cache, device="cuda")
+    K.kvs_score(p, x["q"], x["k"], scores, K.workspace(p))
+    torch.cuda.synchronize()
+    sc = scores.view(s.layers, s.kv_heads, s.n_cache).cpu()
+    got, _ = run_query_select(K, sc, s.layers, s.kv_heads, s.n_cache, s.n_sinks, s.chunk_size, 0.1)
+    want = O.select_queries(O.token_sums_f32(sc.numpy()), s.n_cache, s.n_sinks, s.chunk_size, 0.1)
+    assert all(np.array_equal(a, b) for a, b in zip(got, want))
