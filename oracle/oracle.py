@@ -46,6 +46,17 @@ What it computes, step by step, with the passage each step follows:
               have the same token granularity and can replace the stage-1
               proxy for another pass (refinement); this is that selection.
               Ties go to the lower position; each chunk's list is ascending.
+  global      KV² summary, "무엇과 다른가": the chunks' local scores are gathered
+              into one global tensor, the sinks pinned to the top, and the
+              lowest entries evicted down to the target budget, so each head
+              keeps its own number of positions ("전제와 한계": a headwise
+              compacted cache with a different length per head).  Read as one
+              budget over every (layer, KV head, position); ties by (score
+              descending, unit l*Hkv + g ascending, position ascending).
+  decode      KV² summary, "전제와 한계": serving needs an attention kernel
+              that accepts a different compressed length per head.  One new
+              query token per query head attends its KV head's kept rows with
+              the usual scaled dot product; a head with no kept row yields 0.
 
 Every pin of these functions lives in tests/test_oracle_*.py.
 """
@@ -363,5 +374,66 @@ def select_queries(p: np.ndarray, n_cache: int, n_sinks: int, chunk_size: int,
         cand = np.arange(a, b)
         order = np.lexsort((cand, -p[a:b].astype(np.float64)))
         out.append(np.sort(cand[order[:nq]]).astype(np.int64))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# global eviction with ragged heads (KV² summary, "무엇과 다른가" and
+# "전제와 한계") and decode attention over the result
+# ---------------------------------------------------------------------------
+
+def select_global(score: np.ndarray, total: int, n_sinks: int) -> List[np.ndarray]:
+    """Per unit u = l * Hkv + g, the ascending kept positions: every sink, plus the
+    total - U*S best non-sink entries of the whole tensor by (score desc, u, i)."""
+    s = np.asarray(score, np.float64)
+    L, H, N = s.shape
+    U = L * H
+    s0 = min(n_sinks, N)
+    need = total - U * s0
+    if not (0 <= need <= U * (N - s0)):
+        raise BudgetError("total must lie in [units * n_sinks, units * n_cache]")
+    flat = s.reshape(U, N)[:, s0:]
+    uu, ii = np.meshgrid(np.arange(U), np.arange(s0, N), indexing="ij")
+    order = np.lexsort((ii.ravel(), uu.ravel(), -flat.ravel()))[:need]
+    chosen = np.zeros((U, N - s0), bool)
+    chosen.ravel()[order] = True
+    return [np.concatenate([np.arange(s0), s0 + np.nonzero(chosen[u])[0]]).astype(np.int64)
+            for u in range(U)]
+
+
+def pack_ragged(kept: List[np.ndarray]) -> Tuple[np.ndarray, np.ndarray]:
+    """The lists end to end, and offsets [U + 1] (unit u's list at offsets[u])."""
+    counts = np.array([len(x) for x in kept], np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    flat = np.concatenate(kept).astype(np.int64) if kept else np.zeros(0, np.int64)
+    return flat, offsets
+
+
+def compact_ragged(k: np.ndarray, v: np.ndarray, kept: List[np.ndarray]):
+    """K_out, V_out [sum k_u, d]: unit u's kept rows, unit after unit."""
+    L, H, N, d = k.shape
+    ks = [k[u // H, u % H][kept[u]] for u in range(L * H)]
+    vs = [v[u // H, u % H][kept[u]] for u in range(L * H)]
+    return (np.concatenate(ks) if ks else np.zeros((0, d)),
+            np.concatenate(vs) if vs else np.zeros((0, d)))
+
+
+def decode_attention(q: np.ndarray, k_out: np.ndarray, v_out: np.ndarray, offsets: np.ndarray,
+                     kv_heads: int) -> np.ndarray:
+    """o[l, h] = softmax_j(q[l, h] . k_j / sqrt(d)) v_j over the rows of KV head
+    h // G of layer l in the ragged compacted cache ([L, Hq, d] -> [L, Hq, d])."""
+    q = np.asarray(q, np.float64)
+    L, Hq, d = q.shape
+    G = Hq // kv_heads
+    out = np.zeros((L, Hq, d))
+    for l in range(L):
+        for h in range(Hq):
+            u = l * kv_heads + h // G
+            a, b = int(offsets[u]), int(offsets[u + 1])
+            if b == a:
+                continue
+            kr = np.asarray(k_out[a:b], np.float64)
+            vr = np.asarray(v_out[a:b], np.float64)
+            out[l, h] = softmax_rows((kr @ q[l, h] / math.sqrt(d))[None])[0] @ vr
     return out
 
