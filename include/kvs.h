@@ -148,6 +148,9 @@ int kvs_score(const kvs_problem* p, const void* q, const void* k, float* scores,
  * kept: device int32, packed layer after layer and head after head: the list
  * of (l, g) starts at Hkv * sum_{l'<l} k_l' + g * k_l and has k_l entries.
  * Scores compare as floats (-0 equals +0); NaN orders above +inf.
+ * ws: device workspace of kvs_workspace_bytes(p) bytes, 256-byte aligned; it
+ * is used (and then required, else KVS_E_NULL / KVS_E_WORKSPACE /
+ * KVS_E_ALIGN) only when N - S exceeds 32768 candidates per (l, g).
  */
 int kvs_select(const kvs_problem* p, const float* scores, const int64_t* k_per_layer,
                int32_t* kept, void* ws, size_t ws_bytes, void* stream);
@@ -249,6 +252,70 @@ size_t kvs_query_workspace_bytes(const kvs_problem* p);
 int kvs_query_counts(const kvs_problem* p, double rho, int64_t* counts, int64_t* total);
 int kvs_query_select(const kvs_problem* p, const float* scores, double rho, int32_t* positions,
                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Global eviction (KV² summary, "무엇과 다른가": the chunks' local scores are
+ * gathered into one global tensor, the sinks pinned to the top, and the
+ * lowest entries evicted down to the target budget; "전제와 한계": each head
+ * then keeps its own number of positions).  One budget over every (layer,
+ * KV head, position): each unit u = l * Hkv + g keeps its sinks [0, S), and
+ * the total_budget - L*Hkv*S best non-sink entries of the whole tensor, in the
+ * order (score descending, unit ascending, position ascending), are kept too.
+ *
+ * kvs_select_global: scores device [L, Hkv, N] fp32.  kept: device int32
+ *   [total_budget], unit after unit, each unit's positions ascending (sinks
+ *   first).  offsets: device int64 [L*Hkv + 1]; unit u's list is
+ *   kept[offsets[u] .. offsets[u+1]), offsets[0] = 0 and
+ *   offsets[L*Hkv] = total_budget.  ws: device workspace of at least
+ *   kvs_workspace_bytes(p) bytes, 256-byte aligned.
+ * kvs_compact_ragged: copies row kept[t] of unit u's K and V slab (the
+ *   layout of kvs_problem, kv_row_stride included) to row t of k_out / v_out
+ *   ([total_rows, d] of the problem's dtype, must not overlap K or V), for
+ *   every t in [offsets[u], offsets[u+1]).  kept and offsets as written by
+ *   kvs_select_global with total_rows = offsets[L*Hkv]; an entry of kept
+ *   outside [0, N) leaves its output row untouched.
+ * kvs_compress_global: kvs_score, kvs_select_global and kvs_compact_ragged
+ *   in sequence; one workspace serves all three.
+ * Errors: as kvs_check_problem; KVS_E_SHAPE when L*Hkv*N exceeds 2^31 - 1
+ * (device counts are 32-bit) or total_rows lies outside [0, L*Hkv*N];
+ * KVS_E_BUDGET when total_budget lies outside [L*Hkv*min(S, N), L*Hkv*N];
+ * KVS_E_NULL, KVS_E_ALIGN (kept 4-byte, offsets 8-byte, rows 16-byte, ws
+ * 256-byte), KVS_E_WORKSPACE.
+ */
+int kvs_select_global(const kvs_problem* p, const float* scores, int64_t total_budget,
+                      int32_t* kept, int64_t* offsets, void* ws, size_t ws_bytes, void* stream);
+int kvs_compact_ragged(const kvs_problem* p, const void* k, const void* v, const int32_t* kept,
+                       const int64_t* offsets, int64_t total_rows, void* k_out, void* v_out,
+                       void* stream);
+int kvs_compress_global(const kvs_problem* p, const void* q, const void* k, const void* v,
+                        int64_t total_budget, float* scores, int32_t* kept, int64_t* offsets,
+                        void* k_out, void* v_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Decode attention over a headwise-compacted cache with a different length
+ * per head (KV² summary, "전제와 한계": serving needs an attention kernel that
+ * accepts such a cache).  For every layer l and query head h, with unit
+ * u = l * Hkv + h / G:
+ *     out[l, h, :] = sum_j softmax_j(q[l, h] . k_out[j] / sqrt(d)) v_out[j, :]
+ * over the rows j in [offsets[u], offsets[u+1]) of k_out / v_out; a unit with
+ * no row gives zeros.  One new token per query head: q device [L, Hq, d] of
+ * the problem's dtype; k_out, v_out device [rows, d] of that dtype (e.g.
+ * kvs_compact_ragged's output); offsets device int64 [L*Hkv + 1],
+ * non-decreasing, with sum of the row counts <= max_rows; out device fp32
+ * [L, Hq, d].  Only layers, q_heads, kv_heads, head_dim and dtype of p are
+ * used (the rest must still be valid).  A caller serving one layer at a time
+ * passes a problem with layers = 1 and offsets + l * Hkv (offsets are
+ * absolute row numbers).  ws: device workspace of at least
+ * kvs_decode_workspace_bytes(p, max_rows) bytes, 256-byte aligned.
+ * Errors: as kvs_check_problem; KVS_E_SHAPE (max_rows < 0 or a grid too
+ * large), KVS_E_NULL, KVS_E_ALIGN (q, rows, out 16-byte, offsets 8-byte, ws
+ * 256-byte), KVS_E_WORKSPACE.  Offsets that break the row-count bound give
+ * unspecified values.
+ */
+size_t kvs_decode_workspace_bytes(const kvs_problem* p, int64_t max_rows);
+int kvs_decode_ragged(const kvs_problem* p, const void* q, const void* k_out, const void* v_out,
+                      const int64_t* offsets, int64_t max_rows, float* out, void* ws,
+                      size_t ws_bytes, void* stream);
 
 /*
  * Block append for the block-prefill loop (EpiCache review, "방법: 3단계" (2),

@@ -76,6 +76,16 @@ SIGNATURES = {
     "kvs_query_counts": (c_int32, [ctypes.POINTER(KvsProblem), c_double, P_I64, P_I64]),
     "kvs_query_select": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p, c_double, c_void_p,
                                    c_void_p, c_size_t, c_void_p]),
+    "kvs_select_global": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p, c_int64, c_void_p,
+                                    c_void_p, c_void_p, c_size_t, c_void_p]),
+    "kvs_compact_ragged": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_int64, c_void_p, c_void_p, c_void_p]),
+    "kvs_compress_global": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p, c_void_p, c_void_p,
+                                      c_int64, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_size_t, c_void_p]),
+    "kvs_decode_workspace_bytes": (c_size_t, [ctypes.POINTER(KvsProblem), c_int64]),
+    "kvs_decode_ragged": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
     "kvs_append_rows": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_int64, c_int64,
                                   c_void_p, c_int64, c_int64, c_void_p]),
     "kvs_trace_enable": (c_int32, [c_int32]),

@@ -125,8 +125,19 @@ def kvs_score(p: KvsProblem, q: Tensorish, k: Tensorish, scores: Tensorish, ws: 
                                 _stream(stream)), "kvs_score")
 
 
+def _ws_or_new(p: KvsProblem, ws: Tensorish, ws_bytes: Optional[int], like: Tensorish):
+    """The caller's workspace and its size, or a new one of kvs_workspace_bytes(p)."""
+    if ws is None:
+        ws = torch.empty(max(kvs_workspace_bytes(p), 256), dtype=torch.uint8,
+                         device=like.device if isinstance(like, torch.Tensor) else "cuda")
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    return ws, ws_bytes
+
+
 def kvs_select(p: KvsProblem, scores: Tensorish, k_per_layer: Sequence[int], kept: Tensorish,
-               ws: Tensorish = None, ws_bytes: int = 0, stream=None) -> None:
+               ws: Tensorish = None, ws_bytes: Optional[int] = None, stream=None) -> None:
+    ws, ws_bytes = _ws_or_new(p, ws, ws_bytes, scores)
     _check(_lib.lib().kvs_select(ctypes.byref(p), _dev(scores, "scores"), _i64(k_per_layer),
                                  _dev(kept, "kept"), _dev(ws, "ws"), ws_bytes, _stream(stream)),
            "kvs_select")
@@ -203,6 +214,56 @@ def kvs_query_select(p: KvsProblem, scores: Tensorish, rho: float, positions: Te
     _check(_lib.lib().kvs_query_select(ctypes.byref(p), _dev(scores, "scores"), float(rho),
                                        _dev(positions, "positions"), _dev(ws, "ws"), ws_bytes,
                                        _stream(stream)), "kvs_query_select")
+
+
+def kvs_select_global(p: KvsProblem, scores: Tensorish, total_budget: int, kept: Tensorish,
+                      offsets: Tensorish, ws: Tensorish = None, ws_bytes: Optional[int] = None,
+                      stream=None) -> None:
+    ws, ws_bytes = _ws_or_new(p, ws, ws_bytes, scores)
+    _check(_lib.lib().kvs_select_global(ctypes.byref(p), _dev(scores, "scores"), int(total_budget),
+                                        _dev(kept, "kept"), _dev(offsets, "offsets"),
+                                        _dev(ws, "ws"), ws_bytes, _stream(stream)),
+           "kvs_select_global")
+
+
+def kvs_compact_ragged(p: KvsProblem, k: Tensorish, v: Tensorish, kept: Tensorish,
+                       offsets: Tensorish, total_rows: int, k_out: Tensorish, v_out: Tensorish,
+                       stream=None) -> None:
+    _check(_lib.lib().kvs_compact_ragged(ctypes.byref(p), _dev(k, "k"), _dev(v, "v"),
+                                         _dev(kept, "kept"), _dev(offsets, "offsets"),
+                                         int(total_rows), _dev(k_out, "k_out"),
+                                         _dev(v_out, "v_out"), _stream(stream)),
+           "kvs_compact_ragged")
+
+
+def kvs_compress_global(p: KvsProblem, q: Tensorish, k: Tensorish, v: Tensorish,
+                        total_budget: int, scores: Tensorish, kept: Tensorish, offsets: Tensorish,
+                        k_out: Tensorish, v_out: Tensorish, ws: Tensorish = None,
+                        ws_bytes: Optional[int] = None, stream=None) -> None:
+    ws, ws_bytes = _ws_or_new(p, ws, ws_bytes, k)
+    _check(_lib.lib().kvs_compress_global(
+        ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), int(total_budget),
+        _dev(scores, "scores"), _dev(kept, "kept"), _dev(offsets, "offsets"),
+        _dev(k_out, "k_out"), _dev(v_out, "v_out"), _dev(ws, "ws"), ws_bytes, _stream(stream)),
+        "kvs_compress_global")
+
+
+def kvs_decode_workspace_bytes(p: KvsProblem, max_rows: int) -> int:
+    return int(_lib.lib().kvs_decode_workspace_bytes(ctypes.byref(p), int(max_rows)))
+
+
+def kvs_decode_ragged(p: KvsProblem, q: Tensorish, k_out: Tensorish, v_out: Tensorish,
+                      offsets: Tensorish, max_rows: int, out: Tensorish, ws: Tensorish = None,
+                      ws_bytes: Optional[int] = None, stream=None) -> None:
+    if ws is None:
+        ws = torch.empty(max(kvs_decode_workspace_bytes(p, max_rows), 256), dtype=torch.uint8,
+                         device=q.device)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    _check(_lib.lib().kvs_decode_ragged(ctypes.byref(p), _dev(q, "q"), _dev(k_out, "k_out"),
+                                        _dev(v_out, "v_out"), _dev(offsets, "offsets"),
+                                        int(max_rows), _dev(out, "out"), _dev(ws, "ws"),
+                                        ws_bytes, _stream(stream)), "kvs_decode_ragged")
 
 
 def kvs_append_rows(slabs: int, head_dim: int, dtype: Union[int, torch.dtype], src: Tensorish,

@@ -104,6 +104,83 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const uint8_t* src, in
   }
 }
 
+// Ragged compaction (global eviction): output row t belongs to the unit u
+// with offsets[u] <= t < offsets[u + 1] and is row kept[t] of that unit's
+// slab.  The grid covers the rows; thread 0 finds the workgroup's first unit
+// by binary search and each row walks forward from it (a workgroup's rows
+// rarely cross more than one unit boundary).
+struct RaggedArgs {
+  const uint8_t* kh;
+  const uint8_t* vh;
+  const uint8_t* kt;
+  const uint8_t* vt;
+  const int32_t* kept;
+  const int64_t* offsets;
+  uint8_t* ko;
+  uint8_t* vo;
+  int64_t row_bytes, h_stride, t_stride, t_row0, split, n_cache, total;
+  int32_t units;
+};
+
+template <int LPR>
+__global__ __launch_bounds__(kThreads) void compact_ragged_kernel(RaggedArgs a) {
+  constexpr int RPP = kThreads / LPR;
+  __shared__ int32_t first_unit;
+  const int64_t t0 = (int64_t)blockIdx.x * (RPP * kUnroll);
+  if (threadIdx.x == 0) {
+    int32_t lo = 0, hi = a.units - 1;  // last unit whose list starts at or before t0
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (a.offsets[mid] <= t0) lo = mid;
+      else hi = mid - 1;
+    }
+    first_unit = lo;
+  }
+  __syncthreads();
+  const int piece = threadIdx.x % LPR;
+  const int rsub = threadIdx.x / LPR;
+  int64_t slab[kUnroll], idx[kUnroll];
+  bool ok[kUnroll];
+  int32_t u = first_unit;
+#pragma unroll
+  for (int k = 0; k < kUnroll; ++k) {
+    const int64_t t = t0 + k * RPP + rsub;
+    while (u + 1 < a.units && a.offsets[u + 1] <= t) ++u;
+    const int64_t i = a.kept[min(t, a.total - 1)];
+    ok[k] = t < a.total && i >= 0 && i < a.n_cache;  // rows outside the cache are skipped
+    idx[k] = ok[k] ? i : 0;
+    slab[k] = u;
+  }
+  u32x4 kb[kUnroll], vb[kUnroll];
+#pragma unroll
+  for (int k = 0; k < kUnroll; ++k) {
+    const int64_t i = idx[k];
+    const bool head = i < a.split;
+    const int64_t src = head ? (slab[k] * a.h_stride + i) * a.row_bytes
+                             : (slab[k] * a.t_stride + a.t_row0 + (i - a.split)) * a.row_bytes;
+    kb[k] = __builtin_nontemporal_load((const u32x4*)((head ? a.kh : a.kt) + src + piece * 16));
+    vb[k] = __builtin_nontemporal_load((const u32x4*)((head ? a.vh : a.vt) + src + piece * 16));
+  }
+#pragma unroll
+  for (int k = 0; k < kUnroll; ++k) {
+    if (ok[k]) {
+      const int64_t dst = (t0 + k * RPP + rsub) * a.row_bytes + piece * 16;
+      __builtin_nontemporal_store(kb[k], (u32x4*)(a.ko + dst));
+      __builtin_nontemporal_store(vb[k], (u32x4*)(a.vo + dst));
+    }
+  }
+}
+
+template <int LPR>
+int compact_ragged_lpr(const RaggedArgs& a, hipStream_t st) {
+  constexpr int RPP = kThreads / LPR;
+  const int64_t gx = ceil_div(a.total, RPP * kUnroll);
+  if (gx <= 0 || a.units <= 0) return 0;
+  TraceScope ts("compact_ragged", st);
+  hipLaunchKernelGGL(compact_ragged_kernel<LPR>, dim3((unsigned)gx), dim3(kThreads), 0, st, a);
+  return (int)hipGetLastError();
+}
+
 template <int LPR>
 int compact_lpr(const CompactArgs& a, int64_t units, int32_t k_max, hipStream_t st) {
   constexpr int RPP = kThreads / LPR;
@@ -157,6 +234,34 @@ int launch_compact(const kvs_problem& p, const KvSrc& kv, const int32_t* kept,
     case 128: return compact_lpr<8>(a, units, k_max, st);
     case 256: return compact_lpr<16>(a, units, k_max, st);
     default: return compact_lpr<32>(a, units, k_max, st);
+  }
+}
+
+int launch_compact_ragged(const kvs_problem& p, const KvSrc& kv, const int32_t* kept,
+                          const int64_t* offsets, int64_t total, void* k_out, void* v_out,
+                          void* stream) {
+  RaggedArgs a;
+  a.kh = static_cast<const uint8_t*>(kv.k_head);
+  a.vh = static_cast<const uint8_t*>(kv.v_head);
+  a.kt = static_cast<const uint8_t*>(kv.k_tail);
+  a.vt = static_cast<const uint8_t*>(kv.v_tail);
+  a.h_stride = kv.head_stride;
+  a.t_stride = kv.tail_stride;
+  a.t_row0 = kv.tail_row0;
+  a.split = kv.split;
+  a.kept = kept;
+  a.offsets = offsets;
+  a.ko = static_cast<uint8_t*>(k_out);
+  a.vo = static_cast<uint8_t*>(v_out);
+  a.row_bytes = (int64_t)p.head_dim * (p.dtype == KVS_F32 ? 4 : 2);
+  a.n_cache = p.n_cache;
+  a.total = total;
+  a.units = p.layers * p.kv_heads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (a.row_bytes) {
+    case 128: return compact_ragged_lpr<8>(a, st);
+    case 256: return compact_ragged_lpr<16>(a, st);
+    default: return compact_ragged_lpr<32>(a, st);
   }
 }
 

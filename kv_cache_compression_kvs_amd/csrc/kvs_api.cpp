@@ -159,6 +159,24 @@ int do_score(const kvs_problem& p, const void* q, const KvSrc& kv, float* scores
   return KVS_OK;
 }
 
+// The multi-workgroup select (long caches) needs the caller's workspace.
+int check_select_ws(const kvs_problem& p, const void* ws, size_t ws_bytes) {
+  if (!select_uses_multi(p)) return KVS_OK;
+  if (!ws) return KVS_E_NULL;
+  if (ws_bytes < select_ws_layout(p).bytes) return KVS_E_WORKSPACE;
+  if (!aligned(ws, 256)) return KVS_E_ALIGN;
+  return KVS_OK;
+}
+
+// Global eviction budget: every unit keeps its sinks, at most every position.
+int check_global(const kvs_problem& p, int64_t total) {
+  const int64_t units = (int64_t)p.layers * p.kv_heads;
+  if (units * p.n_cache > INT32_MAX) return KVS_E_SHAPE;  // counts are 32-bit on the device
+  const int64_t s_eff = std::min(p.n_sinks, p.n_cache);
+  if (total < units * s_eff || total > units * p.n_cache) return KVS_E_BUDGET;
+  return KVS_OK;
+}
+
 int enqueue_score(const kvs_problem& p, const void* q, const KvSrc& kv, float* scores, void* ws,
                   void* stream) {
   if (p.n_cache == 0) return KVS_OK;
@@ -190,6 +208,7 @@ int compress(const kvs_problem& p, const void* q, const KvSrc& kv, int64_t total
   if (st) return st;
   st = do_score(p, q, kv, scores, ws, ws_bytes);
   if (st) return st;
+  if ((st = check_select_ws(p, ws, ws_bytes))) return st;
   if ((st = check_src(p, kv, true))) return st;
   if (p.n_cache > 0 && (!kept || !k_out || !v_out)) return KVS_E_NULL;
   if ((kept && !aligned(kept, 4)) || (k_out && !aligned(k_out, 16)) ||
@@ -199,7 +218,7 @@ int compress(const kvs_problem& p, const void* q, const KvSrc& kv, int64_t total
   if (p.n_cache == 0) return KVS_OK;
   st = enqueue_score(p, q, kv, scores, ws, stream);
   if (st) return st;
-  st = to_status(launch_select(p, scores, t, kept, stream));
+  st = to_status(launch_select(p, scores, t, kept, ws, stream));
   if (st) return st;
   if (kmax == 0) return KVS_OK;
   return to_status(launch_compact(p, kv, kept, t, kmax, k_out, v_out, out_row_stride, stream));
@@ -302,7 +321,7 @@ int64_t kvs_num_queries(const kvs_problem* p) {
 
 size_t kvs_workspace_bytes(const kvs_problem* p) {
   if (check(p) != KVS_OK) return 0;
-  return plan_score(*p).ws_bytes;
+  return std::max(plan_score(*p).ws_bytes, select_ws_layout(*p).bytes);
 }
 
 int kvs_layer_budgets(int32_t layers, int64_t total, const double* sens, double alpha,
@@ -322,8 +341,6 @@ int kvs_score(const kvs_problem* p, const void* q, const void* k, float* scores,
 
 int kvs_select(const kvs_problem* p, const float* scores, const int64_t* k_per_layer,
                int32_t* kept, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   int st = check(p);
   if (st) return st;
   LayerTable t;
@@ -332,7 +349,8 @@ int kvs_select(const kvs_problem* p, const float* scores, const int64_t* k_per_l
   if (st) return st;
   if (p->n_cache > 0 && (!scores || !kept)) return KVS_E_NULL;
   if ((scores && !aligned(scores, 4)) || (kept && !aligned(kept, 4))) return KVS_E_ALIGN;
-  return to_status(launch_select(*p, scores, t, kept, stream));
+  if ((st = check_select_ws(*p, ws, ws_bytes))) return st;
+  return to_status(launch_select(*p, scores, t, kept, ws, stream));
 }
 
 int kvs_compact(const kvs_problem* p, const void* k, const void* v, const int32_t* kept,
@@ -427,6 +445,81 @@ int kvs_query_select(const kvs_problem* p, const float* scores, double rho, int3
   if (!aligned(scores, 4) || !aligned(positions, 4) || !aligned(ws, 256)) return KVS_E_ALIGN;
   if ((int64_t)p->layers * p->kv_heads * p->n_cache >= (int64_t(1) << 40)) return KVS_E_SHAPE;
   return to_status(launch_query_select(*p, scores, rho, positions, static_cast<float*>(ws), stream));
+}
+
+int kvs_select_global(const kvs_problem* p, const float* scores, int64_t total_budget,
+                      int32_t* kept, int64_t* offsets, void* ws, size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  if ((st = check_global(*p, total_budget))) return st;
+  if (!offsets || !ws || (p->n_cache > 0 && !scores) || (total_budget > 0 && !kept))
+    return KVS_E_NULL;
+  if (ws_bytes < select_ws_layout(*p).bytes) return KVS_E_WORKSPACE;
+  if ((scores && !aligned(scores, 4)) || (kept && !aligned(kept, 4)) || !aligned(offsets, 8) ||
+      !aligned(ws, 256))
+    return KVS_E_ALIGN;
+  return to_status(launch_select_global(*p, scores, total_budget, kept, offsets, ws, stream));
+}
+
+int kvs_compact_ragged(const kvs_problem* p, const void* k, const void* v, const int32_t* kept,
+                       const int64_t* offsets, int64_t total_rows, void* k_out, void* v_out,
+                       void* stream) {
+  int st = check(p);
+  if (st) return st;
+  if (total_rows < 0 || total_rows > (int64_t)p->layers * p->kv_heads * p->n_cache)
+    return KVS_E_SHAPE;
+  if (!offsets) return KVS_E_NULL;
+  if (total_rows == 0) return KVS_OK;
+  if (!k || !v || !kept || !k_out || !v_out) return KVS_E_NULL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
+      !aligned(kept, 4) || !aligned(offsets, 8))
+    return KVS_E_ALIGN;
+  return to_status(launch_compact_ragged(*p, single_src(*p, k, v), kept, offsets, total_rows,
+                                         k_out, v_out, stream));
+}
+
+int kvs_compress_global(const kvs_problem* p, const void* q, const void* k, const void* v,
+                        int64_t total_budget, float* scores, int32_t* kept, int64_t* offsets,
+                        void* k_out, void* v_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  if ((st = check_global(*p, total_budget))) return st;
+  const KvSrc kv = single_src(*p, k, v);
+  if ((st = do_score(*p, q, kv, scores, ws, ws_bytes))) return st;
+  if ((st = check_src(*p, kv, true))) return st;
+  if (!offsets || !ws) return KVS_E_NULL;
+  if (total_budget > 0 && (!kept || !k_out || !v_out)) return KVS_E_NULL;
+  if (ws_bytes < select_ws_layout(*p).bytes) return KVS_E_WORKSPACE;
+  if ((kept && !aligned(kept, 4)) || !aligned(offsets, 8) || (k_out && !aligned(k_out, 16)) ||
+      (v_out && !aligned(v_out, 16)) || !aligned(ws, 256))
+    return KVS_E_ALIGN;
+  if ((st = enqueue_score(*p, q, kv, scores, ws, stream))) return st;
+  if ((st = to_status(launch_select_global(*p, scores, total_budget, kept, offsets, ws, stream))))
+    return st;
+  if (total_budget == 0) return KVS_OK;
+  return to_status(launch_compact_ragged(*p, kv, kept, offsets, total_budget, k_out, v_out,
+                                         stream));
+}
+
+size_t kvs_decode_workspace_bytes(const kvs_problem* p, int64_t max_rows) {
+  if (check(p) != KVS_OK || max_rows < 0) return 0;
+  return decode_ws_layout(*p, max_rows).bytes;
+}
+
+int kvs_decode_ragged(const kvs_problem* p, const void* q, const void* k_out, const void* v_out,
+                      const int64_t* offsets, int64_t max_rows, float* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  if (max_rows < 0) return KVS_E_SHAPE;
+  const DecodeWs w = decode_ws_layout(*p, max_rows);
+  if (w.slots + 8 > kMaxGrid || (int64_t)p->layers * p->q_heads > kMaxGrid) return KVS_E_SHAPE;
+  if (!q || !offsets || !out || !ws || (max_rows > 0 && (!k_out || !v_out))) return KVS_E_NULL;
+  if (ws_bytes < w.bytes) return KVS_E_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(offsets, 8) || !aligned(ws, 256) ||
+      (k_out && !aligned(k_out, 16)) || (v_out && !aligned(v_out, 16)))
+    return KVS_E_ALIGN;
+  return to_status(launch_decode(*p, q, k_out, v_out, offsets, max_rows, out, ws, stream));
 }
 
 int kvs_append_rows(int32_t slabs, int32_t head_dim, int32_t dtype, const void* src,

@@ -57,15 +57,69 @@ int launch_score_f32(const kvs_problem& p, const ScorePlan& pl, const void* q,
                      const KvSrc& kv, float* scores, void* ws, void* stream);
 int launch_fill(float* dst, int64_t n, float value, void* stream);
 int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t,
-                  int32_t* kept, void* stream);
+                  int32_t* kept, void* ws, void* stream);
+int launch_select_global(const kvs_problem& p, const float* scores, int64_t total,
+                         int32_t* kept, int64_t* offsets, void* ws, void* stream);
 int launch_query_select(const kvs_problem& p, const float* scores, double rho, int32_t* out,
                         float* psum, void* stream);
 int launch_compact(const kvs_problem& p, const KvSrc& kv, const int32_t* kept,
                    const LayerTable& t, int32_t k_max, void* k_out, void* v_out,
                    int64_t out_row_stride, void* stream);
+int launch_compact_ragged(const kvs_problem& p, const KvSrc& kv, const int32_t* kept,
+                          const int64_t* offsets, int64_t total, void* k_out, void* v_out,
+                          void* stream);
+int launch_decode(const kvs_problem& p, const void* q, const void* k, const void* v,
+                  const int64_t* offsets, int64_t max_rows, float* out, void* ws, void* stream);
 int launch_append(int32_t slabs, int64_t row_bytes, const void* src, int64_t src_stride,
                   int64_t src_row0, int64_t n_rows, void* dst, int64_t dst_stride,
                   int64_t dst_row0, void* stream);
+
+// Multi-workgroup radix select: candidates per workgroup, the largest
+// per-unit candidate count the single-workgroup select handles, and the
+// workspace it carves (per-unit mode for long caches, and the global mode).
+constexpr int64_t kSelSpan = 16384;
+constexpr int64_t kSelSingleMax = 32 * 1024;
+
+inline bool select_uses_multi(const kvs_problem& p) {
+  return p.n_cache - (p.n_sinks < p.n_cache ? p.n_sinks : p.n_cache) > kSelSingleMax;
+}
+
+struct SelectWs {
+  size_t off_hist = 0, off_state = 0, off_cnt = 0, off_before = 0, off_ekeep = 0, bytes = 0;
+};
+
+inline SelectWs select_ws_layout(const kvs_problem& p) {
+  auto r256 = [](size_t n) { return (n + 255) & ~size_t(255); };
+  const size_t units = (size_t)p.layers * (size_t)p.kv_heads;
+  const int64_t nc = p.n_cache - (p.n_sinks < p.n_cache ? p.n_sinks : p.n_cache);
+  const size_t nch = (size_t)((nc + kSelSpan - 1) / kSelSpan);
+  SelectWs w;
+  size_t off = 0;
+  w.off_hist = off;
+  off += r256(units * 256 * 4);
+  w.off_state = off;
+  off += r256(units * 16);
+  w.off_cnt = off;
+  off += r256(units * (nch ? nch : 1) * 8);
+  w.off_before = off;
+  off += r256(units * (nch ? nch : 1) * 8);
+  w.off_ekeep = off;
+  off += r256(units * 4);
+  w.bytes = off;
+  return w;
+}
+
+// Decode over a ragged cache: rows per split workgroup, and the workspace
+// (split prefix, per-split partial max / sum / accumulators) for at most
+// max_rows kept rows in total.
+constexpr int kDecodeRows = 256;
+
+struct DecodeWs {
+  int64_t slots = 0;  // split workgroups: ceil(max_rows / kDecodeRows) + units
+  size_t off_sp = 0, off_ml = 0, off_acc = 0, bytes = 0;
+};
+
+DecodeWs decode_ws_layout(const kvs_problem& p, int64_t max_rows);
 
 // Pass-1 tiling constants shared by the planner and the kernels.
 constexpr int kP1Rows = 256;      // query rows per pass-1 workgroup (4 waves x 64)

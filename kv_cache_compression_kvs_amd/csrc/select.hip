@@ -1,13 +1,15 @@
 // Top-k selection per (layer, KV head) (KV² summary, "무엇과 다른가": after the
 // sinks are pinned, the lowest-scoring positions are evicted down to the budget).
 //
-// One 1024-thread workgroup owns one (layer, KV head).  The candidates are the
-// positions [S, N); we need the k - S best under the order (score descending,
-// position ascending), listed ascending together with the sinks [0, S).
+// The candidates are the positions [S, N); we need the k - S best under the
+// order (score descending, position ascending), listed ascending together
+// with the sinks [0, S).  Up to 32K candidates per (layer, KV head), one
+// 1024-thread workgroup owns one (layer, KV head) with its keys cached in
+// LDS; longer caches use the multi-workgroup select further below.
 //
 //  1. Scores become order-preserving 32-bit keys (sign-magnitude flip, -0 read
-//     as +0).  When N - S fits, the keys are cached in LDS; otherwise every
-//     pass re-reads them from global memory (L2 / MALL resident).
+//     as +0), cached in LDS (the query selection's chunks can exceed the cache;
+//     then every pass re-reads them from global memory, L2 / MALL resident).
 //  2. MSB-first radix select in four 8-bit rounds finds the exact key tau of
 //     the (k - S)-th best candidate and e, the number of candidates equal to
 //     tau that must be kept (the lowest positions among the ties).
@@ -33,6 +35,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kItems = 16;                // consecutive candidates per thread in the sweep
 constexpr int kBatch = 8;                 // candidates per thread per histogram iteration
 constexpr int64_t kLdsKeys = 32 * 1024;   // candidates cached in LDS (128 KiB)
+static_assert(kLdsKeys == kSelSingleMax, "longer units go to the multi-workgroup select");
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t b = __float_as_uint(f);
@@ -286,12 +289,399 @@ __global__ __launch_bounds__(kThreads) void query_select_kernel(QueryArgs a) {
   select_body<CACHED>(srow, keys, hw, wsum, pick, out, len, nq, c0);
 }
 
+
+// ---------------------------------------------------------------------------
+// Multi-workgroup radix select.
+//
+// Used when one (layer, KV head) has more candidates than the LDS key cache
+// holds, and for the global eviction over every (layer, KV head) at once (KV²
+// summary, "무엇과 다른가": the chunks' local scores gathered into one tensor,
+// sinks pinned to the top and the lowest entries evicted down to the budget,
+// so that each head ends with its own length, as "전제와 한계" notes).
+//
+// A segment is the candidate set one threshold is found for: one unit's
+// positions [S, N), or (global) every unit's, in (unit, position) order.  Its
+// candidates are cut into spans of kSpan, one workgroup per (span, unit):
+//   init       per segment: histogram cleared, (prefix, rem) = (0, need)
+//   hist, pick four 8-bit digits, most significant first: each span counts
+//              the candidates that match the prefix so far into an LDS
+//              histogram and adds its nonzero bins to the segment's
+//              histogram with integer atomics; one workgroup per segment then
+//              takes the digit where the count from the top reaches rem and
+//              clears the histogram for the next digit.  Afterwards prefix is
+//              tau, the key of the need-th best candidate, and rem is e, the
+//              number of candidates equal to tau that are kept.
+//   count      per span: candidates above tau and equal to tau
+//   scan       per unit: exclusive prefix counts of its spans; in global mode
+//              also each unit's share of the e tied candidates (lower units
+//              first, as the order (score desc, unit, position) says), its
+//              kept count and the start of its list
+//   emit       per span: an ordered block scan places every kept candidate at
+//              its rank in the unit's ascending list
+// Only integer atomics are used, so the result does not depend on scheduling.
+constexpr int kSpan = kSelSpan;  // candidates per workgroup
+static_assert(kSpan == kThreads * kItems, "one span is kItems candidates per thread");
+
+struct MultiArgs {
+  const float* scores;
+  int32_t* kept;
+  int64_t* offsets;   // global mode: [units + 1], start of each unit's list
+  uint32_t* hist;     // [segments][256]
+  uint32_t* state;    // [segments][4]: prefix, rem, done, -
+  uint32_t* cnt;      // [units][nch][2]: (above tau, equal to tau) of each span
+  uint32_t* before;   // [units][nch][2]: the same, summed over the unit's earlier spans
+  uint32_t* ekeep;    // global mode: [units], tau-equal candidates each unit keeps
+  int64_t N, S;       // S is min(n_sinks, N)
+  int64_t nc;         // N - S candidates per unit
+  int64_t need;       // global mode: non-sink entries kept over all units
+  int32_t Hkv, units, nch, global;
+  LayerTable t;
+};
+
+__device__ __forceinline__ int64_t segment_need(const MultiArgs& a, int64_t seg) {
+  return a.global ? a.need : (int64_t)a.t.k[seg / a.Hkv] - a.S;
+}
+
+// Keys of the kItems candidates a thread owns in an order-free pass over a
+// span of len >= 1 candidates at p: candidate j * 4 * kThreads + 4 * tid + q is
+// item 4j + q (idx), so every load instruction of a wave covers 1 KiB.  VEC:
+// p is 16-byte aligned and len a multiple of 4, so each group of four is one
+// 16-byte load.  Loads are clamped into the span; items with idx >= len are
+// not candidates.
+template <bool VEC>
+__device__ __forceinline__ void keys_strided(const float* p, int64_t len, int tid,
+                                             uint32_t (&x)[kItems], int64_t (&idx)[kItems]) {
+#pragma unroll
+  for (int j = 0; j < kItems / 4; ++j) {
+    const int64_t b = (int64_t)j * 4 * kThreads + 4 * tid;
+    if (VEC) {
+      const float4 v = *reinterpret_cast<const float4*>(p + min(b, len - 4));
+      x[4 * j + 0] = order_key(v.x);
+      x[4 * j + 1] = order_key(v.y);
+      x[4 * j + 2] = order_key(v.z);
+      x[4 * j + 3] = order_key(v.w);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[4 * j + q] = order_key(p[min(b + q, len - 1)]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) idx[4 * j + q] = b + q;
+  }
+}
+
+// Keys of the kItems consecutive candidates tid * kItems + j (ordered passes).
+template <bool VEC>
+__device__ __forceinline__ void keys_consecutive(const float* p, int64_t len, int tid,
+                                                 uint32_t (&x)[kItems]) {
+  const int64_t i0 = (int64_t)tid * kItems;
+#pragma unroll
+  for (int j = 0; j < kItems / 4; ++j) {
+    if (VEC) {
+      const float4 v = *reinterpret_cast<const float4*>(p + min(i0 + 4 * j, len - 4));
+      x[4 * j + 0] = order_key(v.x);
+      x[4 * j + 1] = order_key(v.y);
+      x[4 * j + 2] = order_key(v.z);
+      x[4 * j + 3] = order_key(v.w);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[4 * j + q] = order_key(p[min(i0 + 4 * j + q, len - 1)]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void ms_init(MultiArgs a) {
+  const int64_t seg = blockIdx.x;
+  a.hist[seg * 256 + threadIdx.x] = 0u;
+  if (threadIdx.x == 0) {
+    const int64_t count = a.global ? a.nc * a.units : a.nc;
+    const int64_t need = segment_need(a, seg);
+    uint32_t* st = a.state + seg * 4;
+    if (need <= 0) {            // only sinks: no candidate reaches tau = ~0 with e = 0
+      st[0] = 0xFFFFFFFFu;
+      st[1] = 0u;
+      st[2] = 1u;
+    } else if (need >= count) { // every candidate: all keys are >= tau = 0
+      st[0] = 0u;
+      st[1] = (uint32_t)count;
+      st[2] = 1u;
+    } else {
+      st[0] = 0u;
+      st[1] = (uint32_t)need;
+      st[2] = 0u;
+    }
+    st[3] = 0u;
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void ms_hist(MultiArgs a, int shift) {
+  __shared__ uint32_t hw[kWaves * 256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t u = blockIdx.y;
+  const int64_t seg = a.global ? 0 : u;
+  const uint32_t* st = a.state + seg * 4;
+  if (st[2]) return;  // the same for the whole workgroup
+  const uint32_t prefix = st[0];
+  const uint32_t mask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+  for (int b = tid; b < kWaves * 256; b += kThreads) hw[b] = 0u;
+  const int64_t c0 = (int64_t)blockIdx.x * kSpan;
+  const int64_t len = min((int64_t)kSpan, a.nc - c0);
+  uint32_t x[kItems];
+  int64_t idx[kItems];
+  keys_strided<VEC>(a.scores + u * a.N + a.S + c0, len, tid, x, idx);
+  __syncthreads();
+  uint32_t* mine = hw + wave * 256;
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    const bool active = idx[j] < len && (x[j] & mask) == prefix;
+    const uint32_t bin = (x[j] >> shift) & 255u;
+    const uint64_t act = __ballot(active);
+    if (act != 0ull) {
+      const int leader = __ffsll((unsigned long long)act) - 1;
+      const uint32_t lb = __shfl(bin, leader, 64);
+      const uint64_t same = __ballot(active && bin == lb);
+      if (lane == leader) atomicAdd(&mine[lb], (uint32_t)__popcll(same));
+      if (active && bin != lb) atomicAdd(&mine[bin], 1u);
+    }
+  }
+  __syncthreads();
+  if (tid < 256) {
+    uint32_t c = 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) c += hw[w * 256 + tid];
+    if (c) atomicAdd(&a.hist[seg * 256 + tid], c);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void ms_pick(MultiArgs a, int shift) {
+  __shared__ uint32_t wsum[2 * kWaves];
+  const int tid = threadIdx.x;
+  const int64_t seg = blockIdx.x;
+  uint32_t* st = a.state + seg * 4;
+  if (st[2]) return;
+  const uint32_t prefix = st[0];
+  const uint32_t rem = st[1];
+  uint32_t c = 0u;
+  if (tid < 256) {  // thread t holds bin 255 - t: the scan runs from the top bin down
+    uint32_t* h = a.hist + seg * 256 + 255 - tid;
+    c = *h;
+    *h = 0u;        // cleared for the next digit
+  }
+  uint32_t tot;
+  const uint32_t cum = block_scan(c, wsum, &tot);
+  if (tid < 256 && cum >= rem && cum - c < rem) {
+    st[0] = prefix | ((255u - (uint32_t)tid) << shift);
+    st[1] = rem - (cum - c);
+    if (shift == 0) st[2] = 1u;
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void ms_count(MultiArgs a) {
+  __shared__ uint32_t wsum[2 * kWaves];
+  const int tid = threadIdx.x;
+  const int64_t u = blockIdx.y;
+  const uint32_t tau = a.state[(a.global ? 0 : u) * 4];
+  const int64_t c0 = (int64_t)blockIdx.x * kSpan;
+  const int64_t len = min((int64_t)kSpan, a.nc - c0);
+  uint32_t x[kItems];
+  int64_t idx[kItems];
+  keys_strided<VEC>(a.scores + u * a.N + a.S + c0, len, tid, x, idx);
+  uint32_t ngt = 0u, neq = 0u;
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    ngt += idx[j] < len && x[j] > tau;
+    neq += idx[j] < len && x[j] == tau;
+  }
+  uint32_t tot;
+  block_scan((ngt << 16) | neq, wsum, &tot);  // a span's counts fit 16 bits each
+  if (tid == 0) {
+    uint32_t* c = a.cnt + (u * a.nch + blockIdx.x) * 2;
+    c[0] = tot >> 16;
+    c[1] = tot & 0xFFFFu;
+  }
+}
+
+// Per-unit mode: one thread per unit.
+__global__ __launch_bounds__(256) void ms_scan_units(MultiArgs a) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= a.units) return;
+  uint32_t gb = 0u, eb = 0u;
+  for (int64_t c = 0; c < a.nch; ++c) {
+    const int64_t o = (u * a.nch + c) * 2;
+    a.before[o] = gb;
+    a.before[o + 1] = eb;
+    gb += a.cnt[o];
+    eb += a.cnt[o + 1];
+  }
+}
+
+// Global mode: one workgroup walks the units in order.
+__global__ __launch_bounds__(kThreads) void ms_scan_global(MultiArgs a) {
+  __shared__ uint32_t wsum[2 * kWaves];
+  const int tid = threadIdx.x;
+  const uint32_t e = a.state[1];
+  uint64_t carry_eq = 0, carry_k = 0;
+  for (int64_t base = 0; base < a.units; base += kThreads) {
+    const int64_t u = base + tid;
+    uint32_t gt_u = 0u, eq_u = 0u;
+    if (u < a.units) {
+      for (int64_t c = 0; c < a.nch; ++c) {
+        const int64_t o = (u * a.nch + c) * 2;
+        a.before[o] = gt_u;
+        a.before[o + 1] = eq_u;
+        gt_u += a.cnt[o];
+        eq_u += a.cnt[o + 1];
+      }
+    }
+    uint32_t tot_eq;
+    const uint32_t inc_eq = block_scan(eq_u, wsum, &tot_eq);
+    const uint64_t eq_before = carry_eq + (inc_eq - eq_u);
+    const uint32_t e_u = eq_before >= e ? 0u : (uint32_t)min((uint64_t)eq_u, e - eq_before);
+    const uint32_t k_u = u < a.units ? (uint32_t)a.S + gt_u + e_u : 0u;
+    uint32_t tot_k;
+    const uint32_t inc_k = block_scan(k_u, wsum, &tot_k);
+    if (u < a.units) {
+      a.offsets[u] = (int64_t)(carry_k + (inc_k - k_u));
+      a.ekeep[u] = e_u;
+    }
+    carry_eq += tot_eq;
+    carry_k += tot_k;
+  }
+  if (tid == 0) a.offsets[a.units] = (int64_t)carry_k;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void ms_emit(MultiArgs a) {
+  __shared__ uint32_t wsum[2 * kWaves];
+  const int tid = threadIdx.x;
+  const int64_t u = blockIdx.y, c = blockIdx.x;
+  const uint32_t tau = a.state[(a.global ? 0 : u) * 4];
+  uint32_t e_u;
+  int32_t* out;
+  int64_t need_u;
+  if (a.global) {
+    e_u = a.ekeep[u];
+    const int64_t o0 = a.offsets[u];
+    out = a.kept + o0;
+    need_u = a.offsets[u + 1] - o0 - a.S;
+  } else {
+    e_u = a.state[u * 4 + 1];
+    const int64_t l = u / a.Hkv, g = u % a.Hkv, kl = a.t.k[l];
+    out = a.kept + a.t.off[l] + g * kl;
+    need_u = kl - a.S;
+  }
+  if (c == 0)
+    for (int64_t i = tid; i < a.S; i += kThreads) out[i] = (int32_t)i;
+  const int64_t c0 = c * kSpan;
+  const int64_t len = min((int64_t)kSpan, a.nc - c0);
+  if (len <= 0) return;  // no candidate at all (N <= S): only the sinks
+  uint32_t x[kItems];
+  keys_consecutive<VEC>(a.scores + u * a.N + a.S + c0, len, tid, x);
+  const int64_t i0 = (int64_t)tid * kItems;
+  uint32_t ngt = 0u, neq = 0u;
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    ngt += i0 + j < len && x[j] > tau;
+    neq += i0 + j < len && x[j] == tau;
+  }
+  const uint32_t packed = (ngt << 16) | neq;
+  uint32_t tot;
+  const uint32_t excl = block_scan(packed, wsum, &tot) - packed;
+  const uint32_t* bf = a.before + (u * a.nch + c) * 2;
+  uint64_t gt_before = bf[0] + (excl >> 16);
+  uint64_t eq_before = bf[1] + (excl & 0xFFFFu);
+  int32_t* dst = out + a.S;
+  const int64_t val0 = a.S + c0;
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    const int64_t i = i0 + j;
+    // ranks are < need_u by construction; the bound check only keeps a
+    // counting error from ever writing outside this unit's list
+    if (i < len && x[j] > tau) {
+      const uint64_t rank = gt_before + (eq_before < e_u ? eq_before : (uint64_t)e_u);
+      if (rank < (uint64_t)need_u) dst[rank] = (int32_t)(val0 + i);
+      ++gt_before;
+    } else if (i < len && x[j] == tau) {
+      const uint64_t rank = gt_before + eq_before;
+      if (eq_before < e_u && rank < (uint64_t)need_u) dst[rank] = (int32_t)(val0 + i);
+      ++eq_before;
+    }
+  }
+}
+
+template <bool VEC>
+int multi_select(MultiArgs a, int64_t segments, hipStream_t st) {
+  const dim3 spans((unsigned)a.nch, (unsigned)a.units);
+  {
+    TraceScope ts("select_init", st);
+    hipLaunchKernelGGL(ms_init, dim3((unsigned)segments), dim3(256), 0, st, a);
+  }
+  if (a.nc > 0) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      {
+        TraceScope ts("select_hist", st);
+        hipLaunchKernelGGL(ms_hist<VEC>, spans, dim3(kThreads), 0, st, a, shift);
+      }
+      TraceScope ts("select_pick", st);
+      hipLaunchKernelGGL(ms_pick, dim3((unsigned)segments), dim3(kThreads), 0, st, a, shift);
+    }
+    TraceScope ts("select_count", st);
+    hipLaunchKernelGGL(ms_count<VEC>, spans, dim3(kThreads), 0, st, a);
+  }
+  {
+    TraceScope ts("select_scan", st);
+    if (a.global)
+      hipLaunchKernelGGL(ms_scan_global, dim3(1), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(ms_scan_units, dim3((unsigned)ceil_div(a.units, 256)), dim3(256), 0, st, a);
+  }
+  TraceScope ts("select_emit", st);
+  hipLaunchKernelGGL(ms_emit<VEC>, dim3((unsigned)std::max<int64_t>(a.nch, 1), (unsigned)a.units),
+                     dim3(kThreads), 0, st, a);
+  return (int)hipGetLastError();
+}
+
+// Carves the select workspace (layout of select_workspace_bytes) and runs the
+// multi-workgroup select in per-unit or global mode.
+int run_multi(const kvs_problem& p, const float* scores, const LayerTable* t, int64_t need,
+              int32_t* kept, int64_t* offsets, void* ws, hipStream_t st) {
+  const int64_t N = p.n_cache, S = std::min(p.n_sinks, p.n_cache);
+  const int64_t units = (int64_t)p.layers * p.kv_heads;
+  MultiArgs a;
+  a.scores = scores;
+  a.kept = kept;
+  a.offsets = offsets;
+  a.N = N;
+  a.S = S;
+  a.nc = N - S;
+  a.need = need;
+  a.Hkv = p.kv_heads;
+  a.units = (int32_t)units;
+  a.nch = (int32_t)ceil_div(a.nc, kSpan);
+  a.global = t ? 0 : 1;
+  if (t) a.t = *t;
+  const SelectWs w = select_ws_layout(p);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  a.hist = reinterpret_cast<uint32_t*>(base + w.off_hist);
+  a.state = reinterpret_cast<uint32_t*>(base + w.off_state);
+  a.cnt = reinterpret_cast<uint32_t*>(base + w.off_cnt);
+  a.before = reinterpret_cast<uint32_t*>(base + w.off_before);
+  a.ekeep = reinterpret_cast<uint32_t*>(base + w.off_ekeep);
+  const int64_t segments = t ? units : 1;
+  const bool vec = (N % 4 == 0) && (S % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
+  return vec ? multi_select<true>(a, segments, st) : multi_select<false>(a, segments, st);
+}
+
 }  // namespace
 
 int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t,
-                  int32_t* kept, void* stream) {
+                  int32_t* kept, void* ws, void* stream) {
   const int64_t units = (int64_t)p.layers * p.kv_heads;
   if (units <= 0 || p.n_cache <= 0) return 0;
+  const int64_t nc = p.n_cache - std::min(p.n_sinks, p.n_cache);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (select_uses_multi(p)) return run_multi(p, scores, &t, 0, kept, nullptr, ws, st);
   SelArgs a;
   a.scores = scores;
   a.kept = kept;
@@ -299,15 +689,18 @@ int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t
   a.S = p.n_sinks;
   a.Hkv = p.kv_heads;
   a.t = t;
-  const int64_t nc = p.n_cache - std::min(p.n_sinks, p.n_cache);
-  TraceScope ts("select", static_cast<hipStream_t>(stream));
-  if (nc <= kLdsKeys)
-    hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)units), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), a);
-  else
-    hipLaunchKernelGGL(select_kernel<false>, dim3((unsigned)units), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), a);
+  (void)nc;  // <= kLdsKeys here: the candidates fit the LDS key cache
+  TraceScope ts("select", st);
+  hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)units), dim3(kThreads), 0, st, a);
   return (int)hipGetLastError();
+}
+
+int launch_select_global(const kvs_problem& p, const float* scores, int64_t total,
+                         int32_t* kept, int64_t* offsets, void* ws, void* stream) {
+  const int64_t units = (int64_t)p.layers * p.kv_heads;
+  const int64_t S = std::min(p.n_sinks, p.n_cache);
+  return run_multi(p, scores, nullptr, total - units * S, kept, offsets, ws,
+                   static_cast<hipStream_t>(stream));
 }
 
 int launch_query_select(const kvs_problem& p, const float* scores, double rho, int32_t* out,

@@ -101,7 +101,9 @@ def test_workspace_bytes(K):
     rows = 2 * 8 * 5 * 41
     assert ws >= rows * 4 and ws % 256 == 0
     assert K.kvs_workspace_bytes(prob(K, layers=0)) == 0
-    assert K.kvs_workspace_bytes(prob(K, n_cache=3)) == 0
+    # no chunk, so no scoring rows; the global select still keeps its per-unit
+    # histogram and state there
+    assert 0 < K.kvs_workspace_bytes(prob(K, n_cache=3)) <= 4 * 4096
 
 
 @pytest.mark.parametrize("seed", range(25))
@@ -280,3 +282,92 @@ def test_query_select_rejects_bad_arguments(K):
     # every position a sink: nothing to select, nothing touched
     allsink = prob(K, n_cache=4)
     assert h.kvs_query_select(ctypes.byref(allsink), None, 0.1, None, None, 0, None) == 0
+
+
+def test_workspace_covers_the_multi_workgroup_select(K):
+    # per unit: a 256-bin histogram and a state record; per 16K-candidate span
+    # two count pairs
+    p = prob(K, layers=36, q_heads=32, kv_heads=8, n_cache=131072, chunk_size=4096,
+             q_per_chunk=410)
+    units, spans = 36 * 8, 8
+    assert K.kvs_workspace_bytes(p) >= units * (256 * 4 + 16 + spans * 16 + 4)
+
+
+def test_select_requires_workspace_only_for_long_caches(K):
+    h = raw(K)
+    p = prob(K, n_cache=40000, chunk_size=40000)     # 39,996 candidates > 32K
+    ks = (ctypes.c_int64 * 2)(100, 200)
+    ws = K.kvs_workspace_bytes(p)
+    assert h.kvs_select(ctypes.byref(p), FAKE, ks, FAKE, None, 0, None) == 1
+    assert h.kvs_select(ctypes.byref(p), FAKE, ks, FAKE, FAKE, 1024, None) == 6
+    assert h.kvs_select(ctypes.byref(p), FAKE, ks, FAKE, FAKE + 16, ws, None) == 5
+
+
+def test_select_global_rejects_bad_arguments(K):
+    h = raw(K)
+    p = prob(K)                  # 2 layers x 2 KV heads, N = 4300, S = 4
+    ws = K.kvs_workspace_bytes(p)
+
+    def call(total, scores=FAKE, kept=FAKE, offsets=FAKE, w=FAKE, wb=ws, prob_=p):
+        return h.kvs_select_global(ctypes.byref(prob_), scores, total, kept, offsets, w, wb, None)
+
+    assert call(4 * 4 - 1) == 4            # below the sinks of every unit
+    assert call(4 * 4300 + 1) == 4         # above every position
+    assert call(100, offsets=None) == 1
+    assert call(100, w=None) == 1
+    assert call(100, scores=None) == 1
+    assert call(100, wb=1024) == 6          # below the select's own need
+    assert call(100, offsets=FAKE + 4) == 5
+    assert call(100, w=FAKE + 64) == 5
+    big = prob(K, layers=256, kv_heads=8, q_heads=8, n_cache=1 << 20, chunk_size=1 << 20)
+    assert call(10_000, prob_=big, wb=K.kvs_workspace_bytes(big)) == 2   # L*Hkv*N > 2^31 - 1
+
+
+def test_compact_ragged_rejects_bad_arguments(K):
+    h = raw(K)
+    p = prob(K)
+    assert h.kvs_compact_ragged(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == 2
+    assert h.kvs_compact_ragged(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 4 * 4300 + 1, FAKE, FAKE,
+                                None) == 2
+    assert h.kvs_compact_ragged(ctypes.byref(p), FAKE, FAKE, FAKE, None, 10, FAKE, FAKE, None) == 1
+    assert h.kvs_compact_ragged(ctypes.byref(p), FAKE, None, FAKE, FAKE, 10, FAKE, FAKE, None) == 1
+    assert h.kvs_compact_ragged(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 10, FAKE + 8, FAKE,
+                                None) == 5
+    assert h.kvs_compact_ragged(ctypes.byref(p), None, None, None, FAKE, 0, None, None, None) == 0
+
+
+def test_compress_global_rejects_bad_arguments(K):
+    h = raw(K)
+    p = prob(K)
+    ws = K.kvs_workspace_bytes(p)
+
+    def call(total, q=FAKE, v=FAKE, wb=ws):
+        return h.kvs_compress_global(ctypes.byref(p), q, FAKE, v, total, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, wb, None)
+
+    assert call(15) == 4
+    assert call(100, q=None) == 1
+    assert call(100, v=None) == 1
+    assert call(100, wb=1024) == 6
+
+
+def test_decode_workspace_and_errors(K):
+    h = raw(K)
+    p = prob(K)
+    units, G = 4, 4
+    b = K.kvs_decode_workspace_bytes(p, 1000)
+    slots = -(-1000 // 256) + units
+    assert b >= slots * G * (2 + 128) * 4 + (units + 1) * 8
+    assert K.kvs_decode_workspace_bytes(p, -1) == 0
+
+    def call(q=FAKE, k=FAKE, off=FAKE, rows=1000, out=FAKE, w=FAKE, wb=b):
+        return h.kvs_decode_ragged(ctypes.byref(p), q, k, FAKE, off, rows, out, w, wb, None)
+
+    assert call(rows=-1) == 2
+    assert call(q=None) == 1
+    assert call(k=None) == 1
+    assert call(off=None) == 1
+    assert call(out=None) == 1
+    assert call(wb=b - 1) == 6
+    assert call(q=FAKE + 2) == 5
+    assert call(off=FAKE + 4) == 5

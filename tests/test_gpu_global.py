@@ -1,0 +1,233 @@
+"""GPU global eviction with ragged per-head lengths, ragged compaction and decode
+attention over the ragged cache, through the C ABI, against the oracle.
+
+KV² summary, "무엇과 다른가": the chunks' local scores are gathered into one
+tensor, the sinks pinned and the lowest entries evicted to the budget, so each
+head keeps its own number of positions; "전제와 한계": serving such a cache
+needs an attention kernel that accepts a different length per head.
+
+Selection is compared on identical fp32 scores (the GPU's order on fp32 keys
+is the oracle's order on the same values), so the kept lists must be equal.
+Compaction is a bit copy.  Decode is fp32 arithmetic on bf16 / fp32 inputs
+against the float64 oracle: |gpu - oracle| <= 1e-3 * max |v| over the head's
+rows (fp32 dot products of length <= 128 and softmax sums over splits of 256
+rows merged by log-sum-exp keep the error near 1e-5 of that scale).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from workloads import SMALL, gen
+
+from gpu_util import RTOL, assert_scores_close, f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import kv_cache_compression_kvs_amd as pkg
+    return pkg
+
+
+def run_global(K, scores, L, Hkv, N, S, total):
+    p = K.make_problem(L, Hkv, Hkv, 128, N, S, max(N - S, 1), 1, torch.bfloat16)
+    kept = torch.full((max(total, 1),), -7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((L * Hkv + 1,), -9, dtype=torch.int64, device="cuda")
+    K.kvs_select_global(p, scores.reshape(-1).cuda(), total, kept, offsets)
+    torch.cuda.synchronize()
+    off = offsets.cpu().numpy()
+    got = kept.cpu().numpy()
+    return [got[off[u]:off[u + 1]].astype(np.int64) for u in range(L * Hkv)], off
+
+
+GLOBAL = [
+    # (layers, Hkv, N, S, kind, total as a fraction of L*Hkv*N or "sinks"/"all")
+    (2, 2, 300, 4, "uniform", 0.1),
+    (2, 2, 300, 4, "coarse", 0.3),          # ties everywhere: unit then position order
+    (1, 3, 1000, 0, "equal", 0.5),          # every score equal
+    (1, 3, 1000, 0, "equal", "all"),
+    (2, 2, 5000, 4, "sparse", 0.02),        # zeros dominate
+    (2, 2, 6144, 4, "tiny", 0.3),           # denormals and zero
+    (4, 8, 32768, 4, "uniform", 0.05),      # the KV² 32K shape: 16 spans of 16K per unit
+    (2, 3, 40001, 3, "coarse", 0.07),       # unaligned rows: scalar key loads
+    (1, 2, 131072, 4, "uniform", 0.02),
+    (2, 2, 700, 4, "uniform", "sinks"),     # only the sinks
+    (2, 2, 700, 4, "uniform", "all"),       # everything
+    (1, 1, 1, 0, "uniform", "all"),
+    (1, 2, 3, 5, "uniform", "all"),         # N < S: every position is a sink
+]
+
+
+def total_of(L, Hkv, N, S, t):
+    U = L * Hkv
+    if t == "sinks":
+        return U * min(S, N)
+    if t == "all":
+        return U * N
+    return max(U * min(S, N), int(t * U * N))
+
+
+@pytest.mark.parametrize("case", GLOBAL, ids=[str(c) for c in GLOBAL])
+def test_select_global_matches_oracle_exactly(K, case):
+    L, Hkv, N, S, kind, t = case
+    total = total_of(L, Hkv, N, S, t)
+    scores = gen.score_tensor(L * Hkv, N, S, kind, seed=N + L).reshape(L, Hkv, N)
+    got, off = run_global(K, scores, L, Hkv, N, S, total)
+    want = O.select_global(scores.double().numpy(), total, S)
+    assert off[0] == 0 and off[-1] == total
+    for u, (a, b) in enumerate(zip(got, want)):
+        assert np.array_equal(a, b), f"unit {u}: {len(a)} vs {len(b)} kept"
+    counts = np.diff(off)
+    if kind == "uniform" and t not in ("sinks", "all") and L * Hkv > 1:
+        assert len(set(counts.tolist())) > 1   # the heads really are ragged
+
+
+def test_select_global_is_deterministic_and_repeatable(K):
+    L, Hkv, N, S = 2, 4, 20000, 4
+    scores = gen.score_tensor(L * Hkv, N, S, "coarse", seed=3).reshape(L, Hkv, N)
+    a, oa = run_global(K, scores, L, Hkv, N, S, 9000)
+    b, ob = run_global(K, scores, L, Hkv, N, S, 9000)
+    assert np.array_equal(oa, ob) and all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("dt,d,stride", [(torch.bfloat16, 128, 0), (torch.bfloat16, 64, 0),
+                                         (torch.float32, 128, 0), (torch.float32, 64, 0),
+                                         (torch.bfloat16, 128, 1500)])
+def test_compact_ragged_is_bit_exact(K, dt, d, stride):
+    L, Hkv, N, S = 3, 2, 1234, 4
+    scores = gen.score_tensor(L * Hkv, N, S, "uniform", seed=d + stride).reshape(L, Hkv, N)
+    total = 1700
+    kept_lists = O.select_global(scores.double().numpy(), total, S)
+    flat, off = O.pack_ragged(kept_lists)
+    torch.manual_seed(d)
+    rs = stride or N
+    k = torch.randn(L, Hkv, rs, d).to(dt)
+    v = torch.randn(L, Hkv, rs, d).to(dt)
+    p = K.make_problem(L, Hkv, Hkv, d, N, S, N, 1, dt, kv_row_stride=stride)
+    ko = torch.zeros(total, d, dtype=dt, device="cuda")
+    vo = torch.zeros(total, d, dtype=dt, device="cuda")
+    K.kvs_compact_ragged(p, k.cuda(), v.cuda(), torch.from_numpy(flat).int().cuda(),
+                         torch.from_numpy(off).cuda(), total, ko, vo)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.numpy()) if dt == torch.float32 else (lambda t: t.view(torch.int16).numpy())
+    wk, wv = O.compact_ragged(bits(k[:, :, :N]), bits(v[:, :, :N]), kept_lists)
+    assert np.array_equal(bits(ko.cpu()), wk)
+    assert np.array_equal(bits(vo.cpu()), wv)
+
+
+def ragged_cache(counts, d, dt, seed):
+    g = torch.Generator().manual_seed(seed)
+    rows = int(sum(counts))
+    ko = (torch.randn(rows, d, generator=g) * 1.5).to(dt)
+    vo = torch.randn(rows, d, generator=g).to(dt)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return ko, vo, off
+
+
+def check_decode(o, want, vo, off, Hkv):
+    L, Hq, d = want.shape
+    G = Hq // Hkv
+    v64 = vo.double().numpy()
+    for l in range(L):
+        for h in range(Hq):
+            u = l * Hkv + h // G
+            a, b = int(off[u]), int(off[u + 1])
+            scale = float(np.abs(v64[a:b]).max()) if b > a else 1.0
+            err = np.abs(o[l, h] - want[l, h]).max()
+            assert err <= 1e-3 * scale, (l, h, b - a, err, scale)
+
+
+DECODE = [
+    # (layers, Hq, Hkv, d, dtype, counts per unit)
+    (2, 24, 8, 128, torch.bfloat16, None),                 # Llama-3.2-3B heads, random lengths
+    (1, 32, 8, 128, torch.bfloat16, [0, 1, 255, 256, 257, 1000, 3000, 7]),
+    (1, 8, 1, 64, torch.bfloat16, [513]),                  # G = 8: two head groups
+    (1, 4, 4, 128, torch.bfloat16, [5, 0, 0, 300]),         # G = 1, empty heads
+    (1, 6, 2, 64, torch.float32, [300, 17]),
+    (2, 12, 3, 128, torch.float32, [100, 400, 256, 1, 2, 999]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[str(c[:5]) for c in DECODE])
+def test_decode_ragged_matches_oracle(K, case):
+    L, Hq, Hkv, d, dt, counts = case
+    if counts is None:
+        counts = np.random.default_rng(1).integers(4, 2000, size=L * Hkv).tolist()
+    ko, vo, off = ragged_cache(counts, d, dt, seed=len(counts) + d)
+    g = torch.Generator().manual_seed(5)
+    q = (torch.randn(L, Hq, d, generator=g) * 1.5).to(dt)
+    p = K.make_problem(L, Hq, Hkv, d, 16, 0, 16, 1, dt)
+    out = torch.full((L, Hq, d), float("nan"), device="cuda")
+    rows = int(off[-1])
+    K.kvs_decode_ragged(p, q.cuda(), ko.cuda(), vo.cuda(), torch.from_numpy(off).cuda(), rows, out)
+    torch.cuda.synchronize()
+    want = O.decode_attention(q.double().numpy(), ko.double().numpy(), vo.double().numpy(), off, Hkv)
+    check_decode(out.cpu().double().numpy(), want, vo, off, Hkv)
+
+
+def test_decode_one_layer_at_a_time_matches_all_layers(K):
+    L, Hq, Hkv, d = 3, 8, 2, 128
+    counts = [40, 700, 0, 256, 1025, 3]
+    ko, vo, off = ragged_cache(counts, d, torch.bfloat16, seed=11)
+    q = torch.randn(L, Hq, d).bfloat16().cuda()
+    kd, vd, od = ko.cuda(), vo.cuda(), torch.from_numpy(off).cuda()
+    rows = int(off[-1])
+    full = torch.empty(L, Hq, d, device="cuda")
+    K.kvs_decode_ragged(K.make_problem(L, Hq, Hkv, d, 16, 0, 16, 1, torch.bfloat16), q, kd, vd,
+                        od, rows, full)
+    one = K.make_problem(1, Hq, Hkv, d, 16, 0, 16, 1, torch.bfloat16)
+    for l in range(L):
+        part = torch.empty(1, Hq, d, device="cuda")
+        K.kvs_decode_ragged(one, q[l:l + 1].contiguous(), kd, vd, od[l * Hkv:].contiguous(),
+                            rows, part)
+        torch.cuda.synchronize()
+        assert torch.equal(part[0], full[l]), l
+
+
+def test_compress_global_then_decode_small_kv2(K):
+    """Scores, global eviction, ragged compaction and decode on the small KV²
+    workload: scores within tolerance of the oracle, kept lists equal to the
+    oracle's global selection on the GPU's own scores and within the tie band
+    of the float64 scores, rows bit-exact, decode against the oracle."""
+    w = SMALL["kv2_32k"]
+    s = w.shape
+    x = gen.single_inputs(w)
+    L, Hkv, N, d = s.layers, s.kv_heads, s.n_cache, s.head_dim
+    U = L * Hkv
+    total = U * w.keep_per_layer()
+    p = K.make_problem(L, s.q_heads, Hkv, d, N, s.n_sinks, s.chunk_size, s.q_per_chunk,
+                       x["k"].dtype)
+    scores = torch.full((L, Hkv, N), float("nan"), device="cuda")
+    kept = torch.full((total,), -1, dtype=torch.int32, device="cuda")
+    offsets = torch.full((U + 1,), -1, dtype=torch.int64, device="cuda")
+    ko = torch.zeros(total, d, dtype=x["k"].dtype, device="cuda")
+    vo = torch.zeros(total, d, dtype=x["k"].dtype, device="cuda")
+    kd, vd = x["k"].cuda(), x["v"].cuda()
+    K.kvs_compress_global(p, x["q"].cuda(), kd, vd, total, scores, kept, offsets, ko, vo)
+    torch.cuda.synchronize()
+    o = O.scores(f64(x["q"]), f64(x["k"]), s.n_sinks, s.chunk_size, s.q_per_chunk)
+    assert_scores_close(f64(scores), o, "kv2 small")
+    off = offsets.cpu().numpy()
+    got = [kept.cpu().numpy()[off[u]:off[u + 1]].astype(np.int64) for u in range(U)]
+    same = O.select_global(f64(scores), total, s.n_sinks)
+    assert all(np.array_equal(a, b) for a, b in zip(got, same))
+    # against the float64 scores: differences only inside the tie band
+    ref = O.select_global(o, total, s.n_sinks)
+    flat = o.reshape(U, N)[:, s.n_sinks:].ravel()
+    need = total - U * s.n_sinks
+    tau = np.sort(flat)[::-1][need - 1]
+    for u in range(U):
+        for i in set(got[u].tolist()) ^ set(ref[u].tolist()):
+            assert abs(o.reshape(U, N)[u, i] - tau) <= RTOL * tau, (u, i)
+    for u in range(U):
+        idx = torch.from_numpy(got[u]).cuda()
+        assert torch.equal(ko[off[u]:off[u + 1]], kd[u // Hkv, u % Hkv, idx])
+        assert torch.equal(vo[off[u]:off[u + 1]], vd[u // Hkv, u % Hkv, idx])
+    q1 = torch.randn(L, s.q_heads, d, generator=torch.Generator().manual_seed(2)).to(x["k"].dtype)
+    out = torch.empty(L, s.q_heads, d, device="cuda")
+    K.kvs_decode_ragged(p, q1.cuda(), ko, vo, offsets, total, out)
+    torch.cuda.synchronize()
+    want = O.decode_attention(f64(q1), f64(ko), f64(vo), off, Hkv)
+    check_decode(out.cpu().double().numpy(), want, vo.cpu().float(), off, Hkv)
