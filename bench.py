@@ -191,7 +191,9 @@ def main():
                     "traffic": profiled_traffic(w.name, p1_name), "flops_per_launch": per_launch,
                     "avg_launch_ms": round(avg(p1_name, timed_trace), 5)}
     score_ms = tot(p1_name) + tot("score_merge_splits") + tot(p2_name)
-    sc_ms = tot("select") + tot("compact")
+    # the single-workgroup select is "select"; the multi-workgroup one (caches
+    # beyond 32K candidates per head) is the "select_*" kernels
+    sc_ms = sum(tot(k) for k in trace if k == "select" or k.startswith("select_")) + tot("compact")
     kernels = {k: {"avg_ms": round(v["avg_ms"], 5), "count_per_step": v["count"] / bd_steps}
                for k, v in trace.items()}
 
@@ -252,10 +254,74 @@ def main():
             "hbm_frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "kernels": {k: round(v["avg_ms"], 5) for k, v in qtr.items()}}}
 
+    # ---- global eviction, ragged compaction and decode (KV² global budget) ------
+    # Outside the timed step: the same scores evicted under one budget over
+    # every (layer, KV head) (the per-layer total), the kept rows gathered into
+    # a ragged cache, and one decode token attending it.
+    if w.kind != "block_loop" and not args.no_trace:
+        rec["next_rows"] = rec.get("next_rows", {})
+        rec["next_rows"]["f2_global"] = global_row(K, torch, p, s, x, scores, int(sum(kl)) * Hkv,
+                                                   ws, dev)
+
     # ---- float64 oracle on a bounded sample of the same workload ---------------
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, kl)
     print(json.dumps(rec), flush=True)
+
+
+def global_row(K, torch, p, s, x, scores, total, ws, dev):
+    """Times kvs_select_global, kvs_compact_ragged and kvs_decode_ragged on the
+    workload's final scores, with the algorithmic bytes of each."""
+    L, Hq, Hkv, d, N = s.layers, s.q_heads, s.kv_heads, s.head_dim, s.n_cache
+    eb = s.elem_bytes()
+    U = L * Hkv
+    kept = torch.empty(total, dtype=torch.int32, device=dev)
+    offsets = torch.empty(U + 1, dtype=torch.int64, device=dev)
+    ko = torch.empty(total, d, dtype=x["k"].dtype, device=dev)
+    vo = torch.empty(total, d, dtype=x["k"].dtype, device=dev)
+    q1 = torch.randn(L, Hq, d, device=dev).to(x["k"].dtype)
+    out = torch.empty(L, Hq, d, device=dev)
+    dws = torch.empty(max(K.kvs_decode_workspace_bytes(p, total), 256), dtype=torch.uint8,
+                      device=dev)
+
+    def once():
+        K.kvs_select_global(p, scores, total, kept, offsets, ws)
+        K.kvs_compact_ragged(p, x["k"], x["v"], kept, offsets, total, ko, vo)
+        K.kvs_decode_ragged(p, q1, ko, vo, offsets, total, out, dws)
+
+    for _ in range(2):
+        once()
+    torch.cuda.synchronize()
+    K.kvs_trace_summary()
+    K.kvs_trace_only(None)
+    K.kvs_trace_enable(True)
+    reps = 10
+    for _ in range(reps):
+        once()
+    torch.cuda.synchronize()
+    K.kvs_trace_enable(False)
+    tr = K.kvs_trace_summary()
+    counts = (offsets[1:] - offsets[:-1]).cpu()
+
+    def ms(pred):
+        return sum(v["total_ms"] for k, v in tr.items() if pred(k)) / reps
+
+    sel_ms = ms(lambda k: k.startswith("select_"))
+    cmp_ms = ms(lambda k: k == "compact_ragged")
+    dec_ms = ms(lambda k: k.startswith("decode_"))
+    sel_b = 4 * U * N + 4 * total + 8 * (U + 1)
+    cmp_b = total * (2 * d * eb * 2 + 4)
+    dec_b = total * 2 * d * eb + L * Hq * d * (eb + 4)
+
+    def r(b, t):
+        return {"ms": round(t, 5), "algorithmic_bytes": b, "GBps": round(b / (t * 1e-3) / 1e9, 1),
+                "hbm_frac": round(b / (t * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+    return {"total_budget": total, "head_rows_min": int(counts.min()),
+            "head_rows_max": int(counts.max()),
+            "select_global": r(sel_b, sel_ms), "compact_ragged": r(cmp_b, cmp_ms),
+            "select_compact": r(sel_b + cmp_b, sel_ms + cmp_ms), "decode_ragged": r(dec_b, dec_ms),
+            "kernels": {k: round(v["avg_ms"], 5) for k, v in tr.items()}}
 
 
 def profiled_traffic(workload, kernel):

@@ -77,6 +77,26 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint3
   return x;
 }
 
+// Adds one count per active lane to hist[bin] (a histogram in LDS).  Scores
+// cluster, so a wave's active lanes usually fall into a few bins: up to kPeel
+// times, the lowest active lane's bin is counted for every lane that shares
+// it with one atomic; the lanes left after that add individually.
+constexpr int kPeel = 4;
+
+__device__ __forceinline__ void wave_count(uint32_t* hist, bool active, uint32_t bin, int lane) {
+  uint64_t act = __ballot(active);
+#pragma unroll
+  for (int r = 0; r < kPeel; ++r) {
+    if (act == 0ull) return;  // the same on every lane
+    const int leader = __ffsll((unsigned long long)act) - 1;
+    const uint32_t lb = __shfl(bin, leader, 64);
+    const uint64_t same = act & __ballot(bin == lb);
+    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+    act &= ~same;
+  }
+  if ((act >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
+}
+
 // Radix select and ordered sweep over the nc candidates of one (layer, KV
 // head), keys read from the LDS cache (CACHED) or from global memory.  The
 // choice is made once per workgroup so that no key load sits behind a
@@ -117,19 +137,7 @@ __device__ __forceinline__ void select_body(const float* srow, const uint32_t* k
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
           const int64_t i = base + (int64_t)j * kThreads + tid;
-          bool active = i < nc && (xs[j] & mask) == prefix;
-          const uint32_t bin = (xs[j] >> shift) & 255u;
-          // Scores cluster, so most active lanes usually share one bin: count
-          // the first active lane's bin for the whole wave with one atomic,
-          // then the remaining lanes individually.
-          const uint64_t act = __ballot(active);
-          if (act != 0ull) {
-            const int leader = __ffsll((unsigned long long)act) - 1;
-            const uint32_t lb = __shfl(bin, leader, 64);
-            const uint64_t same = __ballot(active && bin == lb);
-            if (lane == leader) atomicAdd(&mine[lb], (uint32_t)__popcll(same));
-            if (active && bin != lb) atomicAdd(&mine[bin], 1u);
-          }
+          wave_count(mine, i < nc && (xs[j] & mask) == prefix, (xs[j] >> shift) & 255u, lane);
         }
       }
       __syncthreads();
@@ -316,8 +324,9 @@ __global__ __launch_bounds__(kThreads) void query_select_kernel(QueryArgs a) {
 //              also each unit's share of the e tied candidates (lower units
 //              first, as the order (score desc, unit, position) says), its
 //              kept count and the start of its list
-//   emit       per span: an ordered block scan places every kept candidate at
-//              its rank in the unit's ascending list
+//   emit       per span: keys staged in LDS by coalesced loads, then an
+//              ordered block scan over kItems consecutive keys per thread places
+//              every kept candidate at its rank in the unit's ascending list
 // Only integer atomics are used, so the result does not depend on scheduling.
 constexpr int kSpan = kSelSpan;  // candidates per workgroup
 static_assert(kSpan == kThreads * kItems, "one span is kItems candidates per thread");
@@ -369,26 +378,6 @@ __device__ __forceinline__ void keys_strided(const float* p, int64_t len, int ti
   }
 }
 
-// Keys of the kItems consecutive candidates tid * kItems + j (ordered passes).
-template <bool VEC>
-__device__ __forceinline__ void keys_consecutive(const float* p, int64_t len, int tid,
-                                                 uint32_t (&x)[kItems]) {
-  const int64_t i0 = (int64_t)tid * kItems;
-#pragma unroll
-  for (int j = 0; j < kItems / 4; ++j) {
-    if (VEC) {
-      const float4 v = *reinterpret_cast<const float4*>(p + min(i0 + 4 * j, len - 4));
-      x[4 * j + 0] = order_key(v.x);
-      x[4 * j + 1] = order_key(v.y);
-      x[4 * j + 2] = order_key(v.z);
-      x[4 * j + 3] = order_key(v.w);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) x[4 * j + q] = order_key(p[min(i0 + 4 * j + q, len - 1)]);
-    }
-  }
-}
-
 __global__ __launch_bounds__(256) void ms_init(MultiArgs a) {
   const int64_t seg = blockIdx.x;
   a.hist[seg * 256 + threadIdx.x] = 0u;
@@ -433,16 +422,7 @@ __global__ __launch_bounds__(kThreads) void ms_hist(MultiArgs a, int shift) {
   uint32_t* mine = hw + wave * 256;
 #pragma unroll
   for (int j = 0; j < kItems; ++j) {
-    const bool active = idx[j] < len && (x[j] & mask) == prefix;
-    const uint32_t bin = (x[j] >> shift) & 255u;
-    const uint64_t act = __ballot(active);
-    if (act != 0ull) {
-      const int leader = __ffsll((unsigned long long)act) - 1;
-      const uint32_t lb = __shfl(bin, leader, 64);
-      const uint64_t same = __ballot(active && bin == lb);
-      if (lane == leader) atomicAdd(&mine[lb], (uint32_t)__popcll(same));
-      if (active && bin != lb) atomicAdd(&mine[bin], 1u);
-    }
+    wave_count(mine, idx[j] < len && (x[j] & mask) == prefix, (x[j] >> shift) & 255u, lane);
   }
   __syncthreads();
   if (tid < 256) {
@@ -554,6 +534,7 @@ __global__ __launch_bounds__(kThreads) void ms_scan_global(MultiArgs a) {
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void ms_emit(MultiArgs a) {
   __shared__ uint32_t wsum[2 * kWaves];
+  __shared__ uint32_t staged[kSpan];
   const int tid = threadIdx.x;
   const int64_t u = blockIdx.y, c = blockIdx.x;
   const uint32_t tau = a.state[(a.global ? 0 : u) * 4];
@@ -576,9 +557,19 @@ __global__ __launch_bounds__(kThreads) void ms_emit(MultiArgs a) {
   const int64_t c0 = c * kSpan;
   const int64_t len = min((int64_t)kSpan, a.nc - c0);
   if (len <= 0) return;  // no candidate at all (N <= S): only the sinks
-  uint32_t x[kItems];
-  keys_consecutive<VEC>(a.scores + u * a.N + a.S + c0, len, tid, x);
+  // coalesced loads into LDS, then each thread takes kItems consecutive keys
+  {
+    uint32_t xs[kItems];
+    int64_t idx[kItems];
+    keys_strided<VEC>(a.scores + u * a.N + a.S + c0, len, tid, xs, idx);
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) staged[idx[j]] = xs[j];  // idx < kSpan
+  }
+  __syncthreads();
   const int64_t i0 = (int64_t)tid * kItems;
+  uint32_t x[kItems];
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) x[j] = staged[i0 + j];
   uint32_t ngt = 0u, neq = 0u;
 #pragma unroll
   for (int j = 0; j < kItems; ++j) {
