@@ -58,6 +58,15 @@ What it computes, step by step, with the passage each step follows:
               query token per query head attends its KV head's kept rows with
               the usual scaled dot product; a head with no kept row yields 0.
 
+  sensitivity EpiCache review, "+α: 레이어별 예산 배분" and Fig. 4(a): the keys
+              a layer computes under block prefill differ from its full-prefill
+              keys by a layer-specific amount, a property of the model that one
+              calibration sample measures; the more a layer's keys move, the
+              more sensitive it is.  Read as: similarity of layer l = mean over
+              (KV head, position) of the cosine between the full-prefill and
+              block-prefill key rows (a zero row has cosine 0), and sensitivity
+              s_l = 1 - similarity_l (the page gives no formula).
+
 Every pin of these functions lives in tests/test_oracle_*.py.
 """
 from __future__ import annotations
@@ -437,3 +446,31 @@ def decode_attention(q: np.ndarray, k_out: np.ndarray, v_out: np.ndarray, offset
             out[l, h] = softmax_rows((kr @ q[l, h] / math.sqrt(d))[None])[0] @ vr
     return out
 
+
+
+# ---------------------------------------------------------------------------
+# layer sensitivity from key similarity (EpiCache review, "+α: 레이어별 예산
+# 배분" and Fig. 4(a))
+# ---------------------------------------------------------------------------
+
+def key_similarity(k_full: np.ndarray, k_block: np.ndarray) -> np.ndarray:
+    """[L]: mean over (KV head, position) of cos(k_full row, k_block row); a
+    pair with a zero row counts as cosine 0.  Inputs [L, Hkv, N, d]."""
+    a = np.asarray(k_full, np.float64)
+    b = np.asarray(k_block, np.float64)
+    L = a.shape[0]
+    out = np.zeros(L)
+    for l in range(L):
+        dot = np.sum(a[l] * b[l], axis=-1)
+        na = np.sqrt(np.sum(a[l] * a[l], axis=-1))
+        nb = np.sqrt(np.sum(b[l] * b[l], axis=-1))
+        den = na * nb
+        cos = np.where(den > 0, dot / np.where(den > 0, den, 1.0), 0.0)
+        out[l] = cos.mean() if cos.size else 0.0
+    return out
+
+
+def sensitivity(similarity: np.ndarray) -> np.ndarray:
+    """s_l = 1 - similarity_l: layers whose keys move more under block prefill
+    are more sensitive to compression."""
+    return 1.0 - np.asarray(similarity, np.float64)
