@@ -263,6 +263,35 @@ def main():
         rec["next_rows"]["f2_global"] = global_row(K, torch, p, s, x, scores, int(sum(kl)) * Hkv,
                                                    ws, dev)
 
+    # ---- layer-sensitivity calibration over the cache's keys (EpiCache) --------
+    # Outside the timed step: the similarity kernel streams two key tensors of
+    # the workload's shape (here the cache's K and V stand in for the full- and
+    # block-prefill keys; the arithmetic and traffic do not depend on values).
+    if w.kind != "block_loop" and not args.no_trace:
+        sim = torch.empty(s.layers, dtype=torch.float64, device=dev)
+        sws = torch.empty(max(K.kvs_similarity_workspace_bytes(p), 256), dtype=torch.uint8,
+                          device=dev)
+        for _ in range(2):
+            K.kvs_key_similarity(p, x["k"], x["v"], sim, sws)
+        torch.cuda.synchronize()
+        K.kvs_trace_summary()
+        K.kvs_trace_only(None)
+        K.kvs_trace_enable(True)
+        reps = 5
+        for _ in range(reps):
+            K.kvs_key_similarity(p, x["k"], x["v"], sim, sws)
+        torch.cuda.synchronize()
+        K.kvs_trace_enable(False)
+        ctr = K.kvs_trace_summary()
+        c_ms = sum(v["total_ms"] for v in ctr.values()) / reps
+        c_bytes = 2 * L * Hkv * s.n_cache * d * eb
+        rec["next_rows"] = rec.get("next_rows", {})
+        rec["next_rows"]["f3_similarity"] = {
+            "ms_per_call": round(c_ms, 5), "algorithmic_bytes": c_bytes,
+            "GBps": round(c_bytes / (c_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(c_bytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "kernels": {k: round(v["avg_ms"], 5) for k, v in ctr.items()}}
+
     # ---- float64 oracle on a bounded sample of the same workload ---------------
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, kl)

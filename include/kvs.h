@@ -318,6 +318,31 @@ int kvs_decode_ragged(const kvs_problem* p, const void* q, const void* k_out, co
                       size_t ws_bytes, void* stream);
 
 /*
+ * Layer sensitivity calibration (EpiCache review, "+α: 레이어별 예산 배분" and
+ * Fig. 4(a): a layer's keys move under block prefill by a layer-specific
+ * amount, a property of the model measured on one calibration sample; layers
+ * whose keys move more are more sensitive and get more budget).
+ *
+ * kvs_key_similarity: similarity[l] = mean over KV heads g and positions
+ *   i < N of cos(k_full[l, g, i, :], k_block[l, g, i, :]), fp32 per row and
+ *   a fixed-order float64 mean (a pair with a zero row counts as cosine 0;
+ *   0 when N = 0).  k_full, k_block: device [L, Hkv, kv_row_stride, d] of the
+ *   problem's dtype (keys of the same tokens from a full prefill and from a
+ *   block-wise prefill).  similarity: device float64 [L].  Uses layers,
+ *   kv_heads, head_dim, n_cache, kv_row_stride and dtype of p.  ws: device
+ *   workspace of kvs_similarity_workspace_bytes(p) bytes, 256-byte aligned.
+ *   Errors: as kvs_check_problem; KVS_E_NULL, KVS_E_WORKSPACE, KVS_E_ALIGN
+ *   (keys 16-byte, similarity 8-byte, ws 256-byte), KVS_E_SHAPE (more than
+ *   65535 slabs).
+ * kvs_sensitivity (host only): sens[l] = 1 - similarity[l], the input of
+ *   kvs_layer_budgets.  KVS_E_BUDGET if a similarity is not in [-1, 1].
+ */
+size_t kvs_similarity_workspace_bytes(const kvs_problem* p);
+int kvs_key_similarity(const kvs_problem* p, const void* k_full, const void* k_block,
+                       double* similarity, void* ws, size_t ws_bytes, void* stream);
+int kvs_sensitivity(int32_t layers, const double* similarity, double* sens);
+
+/*
  * Block append for the block-prefill loop (EpiCache review, "방법: 3단계" (2),
  * Fig. 1(b)): for each of `slabs` (layer, KV head) slabs copies rows
  * [src_row0, src_row0 + n_rows) of src (slab stride src_row_stride rows) to

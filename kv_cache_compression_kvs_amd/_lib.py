@@ -86,6 +86,10 @@ SIGNATURES = {
     "kvs_decode_workspace_bytes": (c_size_t, [ctypes.POINTER(KvsProblem), c_int64]),
     "kvs_decode_ragged": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "kvs_similarity_workspace_bytes": (c_size_t, [ctypes.POINTER(KvsProblem)]),
+    "kvs_key_similarity": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]),
+    "kvs_sensitivity": (c_int32, [c_int32, P_F64, P_F64]),
     "kvs_append_rows": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_int64, c_int64,
                                   c_void_p, c_int64, c_int64, c_void_p]),
     "kvs_trace_enable": (c_int32, [c_int32]),

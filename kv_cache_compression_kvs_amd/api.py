@@ -266,6 +266,33 @@ def kvs_decode_ragged(p: KvsProblem, q: Tensorish, k_out: Tensorish, v_out: Tens
                                         ws_bytes, _stream(stream)), "kvs_decode_ragged")
 
 
+def kvs_similarity_workspace_bytes(p: KvsProblem) -> int:
+    return int(_lib.lib().kvs_similarity_workspace_bytes(ctypes.byref(p)))
+
+
+def kvs_key_similarity(p: KvsProblem, k_full: Tensorish, k_block: Tensorish,
+                       similarity: Tensorish, ws: Tensorish = None,
+                       ws_bytes: Optional[int] = None, stream=None) -> None:
+    """similarity: a float64 GPU tensor of p.layers elements."""
+    if ws is None:
+        ws = torch.empty(max(kvs_similarity_workspace_bytes(p), 256), dtype=torch.uint8,
+                         device=similarity.device)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    _check(_lib.lib().kvs_key_similarity(ctypes.byref(p), _dev(k_full, "k_full"),
+                                         _dev(k_block, "k_block"), _dev(similarity, "similarity"),
+                                         _dev(ws, "ws"), ws_bytes, _stream(stream)),
+           "kvs_key_similarity")
+
+
+def kvs_sensitivity(similarity: Sequence[float]) -> np.ndarray:
+    """Host: 1 - similarity per layer."""
+    n = len(similarity)
+    out = (ctypes.c_double * n)()
+    _check(_lib.lib().kvs_sensitivity(n, _f64(similarity), out), "kvs_sensitivity")
+    return np.array(out[:], dtype=np.float64)
+
+
 def kvs_append_rows(slabs: int, head_dim: int, dtype: Union[int, torch.dtype], src: Tensorish,
                     src_row_stride: int, src_row0: int, n_rows: int, dst: Tensorish,
                     dst_row_stride: int, dst_row0: int, stream=None) -> None:

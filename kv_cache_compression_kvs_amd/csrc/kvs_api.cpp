@@ -522,6 +522,35 @@ int kvs_decode_ragged(const kvs_problem* p, const void* q, const void* k_out, co
   return to_status(launch_decode(*p, q, k_out, v_out, offsets, max_rows, out, ws, stream));
 }
 
+size_t kvs_similarity_workspace_bytes(const kvs_problem* p) {
+  if (check(p) != KVS_OK) return 0;
+  return round256(sizeof(float) * (size_t)p->layers * p->kv_heads *
+                  (size_t)std::max<int64_t>(cdiv(p->n_cache, kSimRows), 1));
+}
+
+int kvs_key_similarity(const kvs_problem* p, const void* k_full, const void* k_block,
+                       double* similarity, void* ws, size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  if (!similarity || !ws || (p->n_cache > 0 && (!k_full || !k_block))) return KVS_E_NULL;
+  if (ws_bytes < kvs_similarity_workspace_bytes(p)) return KVS_E_WORKSPACE;
+  if (!aligned(similarity, 8) || !aligned(ws, 256) || (k_full && !aligned(k_full, 16)) ||
+      (k_block && !aligned(k_block, 16)))
+    return KVS_E_ALIGN;
+  if (cdiv(p->n_cache, kSimRows) > kMaxGrid || (int64_t)p->layers * p->kv_heads > 65535)
+    return KVS_E_SHAPE;
+  return to_status(launch_similarity(*p, k_full, k_block, similarity, ws, stream));
+}
+
+int kvs_sensitivity(int32_t layers, const double* similarity, double* sens) {
+  if (!similarity || !sens) return KVS_E_NULL;
+  if (layers < 1 || layers > KVS_MAX_LAYERS) return KVS_E_SHAPE;
+  for (int l = 0; l < layers; ++l)
+    if (!(similarity[l] >= -1.0 && similarity[l] <= 1.0)) return KVS_E_BUDGET;
+  for (int l = 0; l < layers; ++l) sens[l] = 1.0 - similarity[l];
+  return KVS_OK;
+}
+
 int kvs_append_rows(int32_t slabs, int32_t head_dim, int32_t dtype, const void* src,
                     int64_t src_row_stride, int64_t src_row0, int64_t n_rows, void* dst,
                     int64_t dst_row_stride, int64_t dst_row0, void* stream) {

@@ -70,6 +70,8 @@ int launch_compact_ragged(const kvs_problem& p, const KvSrc& kv, const int32_t* 
                           void* stream);
 int launch_decode(const kvs_problem& p, const void* q, const void* k, const void* v,
                   const int64_t* offsets, int64_t max_rows, float* out, void* ws, void* stream);
+int launch_similarity(const kvs_problem& p, const void* k_full, const void* k_block,
+                      double* similarity, void* ws, void* stream);
 int launch_append(int32_t slabs, int64_t row_bytes, const void* src, int64_t src_stride,
                   int64_t src_row0, int64_t n_rows, void* dst, int64_t dst_stride,
                   int64_t dst_row0, void* stream);
@@ -120,6 +122,10 @@ struct DecodeWs {
 };
 
 DecodeWs decode_ws_layout(const kvs_problem& p, int64_t max_rows);
+
+// Key similarity: rows of one slab per workgroup (its partial sum is one
+// float of workspace).
+constexpr int64_t kSimRows = 1024;
 
 // Pass-1 tiling constants shared by the planner and the kernels.
 constexpr int kP1Rows = 256;      // query rows per pass-1 workgroup (4 waves x 64)

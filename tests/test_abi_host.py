@@ -371,3 +371,29 @@ def test_decode_workspace_and_errors(K):
     assert call(wb=b - 1) == 6
     assert call(q=FAKE + 2) == 5
     assert call(off=FAKE + 4) == 5
+
+
+def test_sensitivity_host_function(K):
+    sim = [0.99, 0.5, -0.25, 1.0]
+    assert K.kvs_sensitivity(sim).tolist() == O.sensitivity(np.array(sim)).tolist()
+    for bad in ([1.5], [float("nan")], [-1.01]):
+        with pytest.raises(K.KvsError) as e:
+            K.kvs_sensitivity(bad)
+        assert e.value.status == 4
+
+
+def test_key_similarity_rejects_bad_arguments(K):
+    h = raw(K)
+    p = prob(K)
+    wb = K.kvs_similarity_workspace_bytes(p)
+    assert wb >= 2 * 2 * 5 * 4       # one float per 1024-row block of each slab
+
+    def call(a=FAKE, b=FAKE, out=FAKE, w=FAKE, n=wb):
+        return h.kvs_key_similarity(ctypes.byref(p), a, b, out, w, n, None)
+
+    assert call(a=None) == 1
+    assert call(out=None) == 1
+    assert call(w=None) == 1
+    assert call(n=wb - 1) == 6
+    assert call(out=FAKE + 4) == 5
+    assert call(b=FAKE + 8) == 5

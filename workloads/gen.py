@@ -307,6 +307,37 @@ def sensitivities(w: Workload, seed: Optional[int] = None) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# layer-sensitivity calibration: keys of one sample from a full prefill and
+# from a block-wise prefill
+# --------------------------------------------------------------------------
+
+def calibration_keys(shape: ScoreShape, n_tokens: int, seed: int = 0, device="cpu",
+                     kv_row_stride: int = 0) -> Dict[str, torch.Tensor]:
+    """k_full, k_block [L, Hkv, kv_row_stride or n_tokens, d] and drift [L].
+
+    Full-prefill keys are Gaussian plus 4 outlier channels per (layer, KV
+    head); the block-prefill keys of the same tokens add noise of a seeded
+    per-layer size drift[l] ~ U[0.05, 0.8] (a fixed property of each layer).
+    Rows past n_tokens (when a row stride is given) are zero.
+    """
+    dt = storage_dtype(shape)
+    L, Hkv, d = shape.layers, shape.kv_heads, shape.head_dim
+    rows = kv_row_stride or n_tokens
+    rs = np.random.Generator(np.random.Philox(_seed(seed, "calib", "drift", L)))
+    drift = rs.uniform(0.05, 0.8, size=L)
+    kf = torch.zeros(L, Hkv, rows, d, dtype=dt, device=device)
+    kb = torch.zeros(L, Hkv, rows, d, dtype=dt, device=device)
+    for l in range(L):
+        for gi in range(Hkv):
+            g = _gen(device, seed, "calib", "k", l, gi, n_tokens, d)
+            base = torch.randn(n_tokens, d, generator=g, device=device) + _outliers(d, 4, g, device)
+            noise = torch.randn(n_tokens, d, generator=g, device=device)
+            kf[l, gi, :n_tokens] = _store(base, dt)
+            kb[l, gi, :n_tokens] = _store(base + float(drift[l]) * noise, dt)
+    return {"k_full": kf, "k_block": kb, "drift": drift}
+
+
+# --------------------------------------------------------------------------
 # inputs for the selection and compaction kernels in isolation
 # --------------------------------------------------------------------------
 
