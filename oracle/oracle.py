@@ -67,6 +67,18 @@ What it computes, step by step, with the passage each step follows:
               block-prefill key rows (a zero row has cosine 0), and sensitivity
               s_l = 1 - similarity_l (the page gives no formula).
 
+  episodes    EpiCache review, "방법: 3단계" (1) and (3), Fig. 3(a) and (c): the
+              history's segments are embedded and clustered by K-means into E
+              episodes; each episode's medoid segment is its representative;
+              a new question's embedding is matched to the closest episode.
+              Read as Lloyd's algorithm with squared Euclidean distance from
+              given initial centroids (ties to the lower cluster, an empty
+              cluster keeps its centroid), a fixed number of rounds of
+              (assign, update) followed by a final assignment; the medoid is
+              the member with the least sum of Euclidean distances to the
+              other members of its cluster (ties to the lower index); matching
+              is the nearest centroid.
+
 Every pin of these functions lives in tests/test_oracle_*.py.
 """
 from __future__ import annotations
@@ -474,3 +486,60 @@ def sensitivity(similarity: np.ndarray) -> np.ndarray:
     """s_l = 1 - similarity_l: layers whose keys move more under block prefill
     are more sensitive to compression."""
     return 1.0 - np.asarray(similarity, np.float64)
+
+
+# ---------------------------------------------------------------------------
+# episode clustering and matching (EpiCache review, "방법: 3단계" (1) and (3))
+# ---------------------------------------------------------------------------
+
+def nearest_centroid(x: np.ndarray, centroids: np.ndarray) -> np.ndarray:
+    """Index of the centroid at the least squared Euclidean distance from each
+    row of x, ties to the lower index."""
+    x = np.asarray(x, np.float64)
+    c = np.asarray(centroids, np.float64)
+    d2 = ((x[:, None, :] - c[None, :, :]) ** 2).sum(-1)
+    return np.argmin(d2, axis=1).astype(np.int64)
+
+
+def kmeans(x: np.ndarray, init: np.ndarray, rounds: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Lloyd's algorithm: `rounds` times assign every point to its nearest
+    centroid and move each centroid to the mean of its points (an empty
+    cluster keeps its centroid); then assign once more.  Returns (centroids,
+    assignment)."""
+    x = np.asarray(x, np.float64)
+    c = np.array(init, np.float64)
+    for _ in range(rounds):
+        a = nearest_centroid(x, c)
+        for e in range(c.shape[0]):
+            members = x[a == e]
+            if len(members):
+                c[e] = members.mean(axis=0)
+    return c, nearest_centroid(x, c)
+
+
+def medoids(x: np.ndarray, assign: np.ndarray, clusters: int) -> np.ndarray:
+    """Per cluster, the member whose summed Euclidean distance to the
+    cluster's members is least (ties to the lower index); -1 for an empty
+    cluster."""
+    x = np.asarray(x, np.float64)
+    assign = np.asarray(assign)
+    out = np.full(clusters, -1, np.int64)
+    for e in range(clusters):
+        idx = np.nonzero(assign == e)[0]
+        if len(idx) == 0:
+            continue
+        pts = x[idx]
+        total = np.sqrt(((pts[:, None, :] - pts[None, :, :]) ** 2).sum(-1)).sum(1)
+        out[e] = idx[int(np.argmin(total))]
+    return out
+
+
+def medoid_totals(x: np.ndarray, assign: np.ndarray) -> np.ndarray:
+    """Each point's summed Euclidean distance to the members of its cluster."""
+    x = np.asarray(x, np.float64)
+    assign = np.asarray(assign)
+    out = np.zeros(len(x))
+    for i in range(len(x)):
+        same = x[assign == assign[i]]
+        out[i] = np.sqrt(((same - x[i]) ** 2).sum(-1)).sum()
+    return out
