@@ -292,6 +292,15 @@ def main():
             "hbm_frac": round(c_bytes / (c_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "kernels": {k: round(v["avg_ms"], 5) for k, v in ctr.items()}}
 
+    # ---- episode clustering and matching (EpiCache), on the episodic workload --
+    # Outside the timed step: 2048 unit-norm segment embeddings of width 1024
+    # (a 90K-token history in segments of about 45 tokens) clustered into the
+    # workload's E episodes by 10 Lloyd rounds, the medoid of each episode, and
+    # 64 questions matched to episodes.
+    if w.kind == "episodic" and not args.no_trace:
+        rec["next_rows"] = rec.get("next_rows", {})
+        rec["next_rows"]["f4_episodes"] = episode_row(K, torch, gen, w.episodes, dev)
+
     # ---- float64 oracle on a bounded sample of the same workload ---------------
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, kl)
@@ -351,6 +360,51 @@ def global_row(K, torch, p, s, x, scores, total, ws, dev):
             "select_global": r(sel_b, sel_ms), "compact_ragged": r(cmp_b, cmp_ms),
             "select_compact": r(sel_b + cmp_b, sel_ms + cmp_ms), "decode_ragged": r(dec_b, dec_ms),
             "kernels": {k: round(v["avg_ms"], 5) for k, v in tr.items()}}
+
+
+def episode_row(K, torch, gen, E, dev):
+    n, dim, rounds = 2048, 1024, 10
+    emb = gen.episode_embeddings(n, dim, E, seed=0)
+    x = emb["x"].to(dev)
+    init = emb["x"][emb["init_index"]].contiguous().to(dev)
+    q = emb["q"].to(dev)
+    cent = torch.empty_like(init)
+    assign = torch.empty(n, dtype=torch.int32, device=dev)
+    med = torch.empty(E, dtype=torch.int32, device=dev)
+    totals = torch.empty(n, device=dev)
+    ep = torch.empty(q.shape[0], dtype=torch.int32, device=dev)
+
+    def once():
+        K.kvs_kmeans(x, init, rounds, cent, assign)
+        K.kvs_medoids(x, assign, E, med, totals)
+        K.kvs_match_episodes(q, cent, ep)
+
+    for _ in range(2):
+        once()
+    torch.cuda.synchronize()
+    K.kvs_trace_summary()
+    K.kvs_trace_only(None)
+    K.kvs_trace_enable(True)
+    reps = 5
+    for _ in range(reps):
+        once()
+    torch.cuda.synchronize()
+    K.kvs_trace_enable(False)
+    tr = K.kvs_trace_summary()
+    a = assign.cpu()
+    sizes = torch.bincount(a.long(), minlength=E)
+    same_pairs = int((sizes.double() ** 2).sum())
+    medoid_flops = 3 * dim * same_pairs          # subtract and fused multiply-add per element
+    med_ms = tr["medoid_total"]["avg_ms"] if "medoid_total" in tr else None
+    return {"segments": n, "dim": dim, "episodes": E, "lloyd_rounds": rounds,
+            "ms_total": round(sum(v["total_ms"] for v in tr.values()) / reps, 5),
+            "medoid_total_ms": round(med_ms, 5) if med_ms else None,
+            "medoid_TFLOPs": round(medoid_flops / (med_ms * 1e-3) / 1e12, 2) if med_ms else None,
+            "medoid_fp32_frac": round(medoid_flops / (med_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)
+            if med_ms else None,
+            "labels_recovered": bool(torch.equal(a.long(), emb["labels"])),
+            "kernels": {k: {"avg_ms": round(v["avg_ms"], 5), "count_per_call": v["count"] / reps}
+                        for k, v in tr.items()}}
 
 
 def profiled_traffic(workload, kernel):

@@ -343,6 +343,39 @@ int kvs_key_similarity(const kvs_problem* p, const void* k_full, const void* k_b
 int kvs_sensitivity(int32_t layers, const double* similarity, double* sens);
 
 /*
+ * Episode clustering and matching (EpiCache review, "방법: 3단계" (1) and (3),
+ * Fig. 3(a) and (c): the history's segments are embedded and clustered by
+ * K-means into E episodes, each represented by its medoid segment; a new
+ * question's embedding picks the closest episode).  Embeddings are fp32 rows
+ * of dim floats, dim a multiple of 4 in [4, 2048]; 1 <= clusters <= 16.
+ *
+ * kvs_kmeans: Lloyd's algorithm from init (device [clusters, dim]): `rounds`
+ *   times, every point takes the centroid at the least squared Euclidean
+ *   distance (ties to the lower one) and each centroid moves to the mean of
+ *   its points (an empty cluster keeps its centroid); then one more
+ *   assignment.  x: device [n, dim]; centroids: device [clusters, dim] out
+ *   (may equal init); assign: device int32 [n] out.  ws: device workspace of
+ *   kvs_kmeans_workspace_bytes(n, dim, clusters) bytes (needed when n > 0 and
+ *   rounds > 0), 256-byte aligned.
+ * kvs_medoids: totals[i] = sum of Euclidean distances from point i to the
+ *   points of its cluster (device fp32 [n] out); medoid[e] = the member of
+ *   cluster e with the least total, ties to the lower index, -1 if empty
+ *   (device int32 [clusters] out).  assign: device int32 [n] in [0, clusters).
+ * kvs_match_episodes: episode[j] = the centroid nearest to query row j (as in
+ *   the assignment), q: device [m, dim], episode: device int32 [m].
+ * Errors: KVS_E_SHAPE (sizes above), KVS_E_NULL, KVS_E_ALIGN (rows 16-byte,
+ * int32 arrays 4-byte, ws 256-byte), KVS_E_WORKSPACE.
+ */
+size_t kvs_kmeans_workspace_bytes(int64_t n, int64_t dim, int32_t clusters);
+int kvs_kmeans(const float* x, int64_t n, int64_t dim, int32_t clusters, const float* init,
+               int32_t rounds, float* centroids, int32_t* assign, void* ws, size_t ws_bytes,
+               void* stream);
+int kvs_medoids(const float* x, int64_t n, int64_t dim, const int32_t* assign, int32_t clusters,
+                int32_t* medoid, float* totals, void* stream);
+int kvs_match_episodes(const float* q, int64_t m, int64_t dim, const float* centroids,
+                       int32_t clusters, int32_t* episode, void* stream);
+
+/*
  * Block append for the block-prefill loop (EpiCache review, "방법: 3단계" (2),
  * Fig. 1(b)): for each of `slabs` (layer, KV head) slabs copies rows
  * [src_row0, src_row0 + n_rows) of src (slab stride src_row_stride rows) to

@@ -293,6 +293,42 @@ def kvs_sensitivity(similarity: Sequence[float]) -> np.ndarray:
     return np.array(out[:], dtype=np.float64)
 
 
+def kvs_kmeans_workspace_bytes(n: int, dim: int, clusters: int) -> int:
+    return int(_lib.lib().kvs_kmeans_workspace_bytes(n, dim, clusters))
+
+
+def kvs_kmeans(x: Tensorish, init: Tensorish, rounds: int, centroids: Tensorish,
+               assign: Tensorish, ws: Tensorish = None, ws_bytes: Optional[int] = None,
+               stream=None) -> None:
+    """x [n, dim] and init [clusters, dim] fp32 GPU tensors; writes centroids and assign."""
+    n, dim = x.shape
+    clusters = init.shape[0]
+    if ws is None:
+        ws = torch.empty(max(kvs_kmeans_workspace_bytes(n, dim, clusters), 256),
+                         dtype=torch.uint8, device=x.device)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    _check(_lib.lib().kvs_kmeans(_dev(x, "x"), n, dim, clusters, _dev(init, "init"), int(rounds),
+                                 _dev(centroids, "centroids"), _dev(assign, "assign"),
+                                 _dev(ws, "ws"), ws_bytes, _stream(stream)), "kvs_kmeans")
+
+
+def kvs_medoids(x: Tensorish, assign: Tensorish, clusters: int, medoid: Tensorish,
+                totals: Tensorish, stream=None) -> None:
+    n, dim = x.shape
+    _check(_lib.lib().kvs_medoids(_dev(x, "x"), n, dim, _dev(assign, "assign"), clusters,
+                                  _dev(medoid, "medoid"), _dev(totals, "totals"),
+                                  _stream(stream)), "kvs_medoids")
+
+
+def kvs_match_episodes(q: Tensorish, centroids: Tensorish, episode: Tensorish,
+                       stream=None) -> None:
+    m, dim = q.shape
+    _check(_lib.lib().kvs_match_episodes(_dev(q, "q"), m, dim, _dev(centroids, "centroids"),
+                                         centroids.shape[0], _dev(episode, "episode"),
+                                         _stream(stream)), "kvs_match_episodes")
+
+
 def kvs_append_rows(slabs: int, head_dim: int, dtype: Union[int, torch.dtype], src: Tensorish,
                     src_row_stride: int, src_row0: int, n_rows: int, dst: Tensorish,
                     dst_row_stride: int, dst_row0: int, stream=None) -> None:

@@ -551,6 +551,54 @@ int kvs_sensitivity(int32_t layers, const double* similarity, double* sens) {
   return KVS_OK;
 }
 
+namespace kvs {
+namespace {
+int check_embed(int64_t n, int64_t dim, int32_t clusters) {
+  if (n < 0 || n > INT32_MAX || dim < 4 || dim > kMaxEmbedDim || dim % 4 != 0) return KVS_E_SHAPE;
+  if (clusters < 1 || clusters > kMaxClusters) return KVS_E_SHAPE;
+  return KVS_OK;
+}
+}  // namespace
+}  // namespace kvs
+
+size_t kvs_kmeans_workspace_bytes(int64_t n, int64_t dim, int32_t clusters) {
+  if (check_embed(n, dim, clusters)) return 0;
+  return kmeans_ws_bytes(n, dim, clusters);
+}
+
+int kvs_kmeans(const float* x, int64_t n, int64_t dim, int32_t clusters, const float* init,
+               int32_t rounds, float* centroids, int32_t* assign, void* ws, size_t ws_bytes,
+               void* stream) {
+  if (int st = check_embed(n, dim, clusters)) return st;
+  if (rounds < 0) return KVS_E_SHAPE;
+  if (!init || !centroids || (n > 0 && (!x || !assign)) || (n > 0 && rounds > 0 && !ws))
+    return KVS_E_NULL;
+  if (n > 0 && rounds > 0 && ws_bytes < kmeans_ws_bytes(n, dim, clusters)) return KVS_E_WORKSPACE;
+  if (!aligned(init, 16) || !aligned(centroids, 16) || (x && !aligned(x, 16)) ||
+      (assign && !aligned(assign, 4)) || (ws && !aligned(ws, 256)))
+    return KVS_E_ALIGN;
+  return to_status(launch_kmeans(x, n, dim, clusters, init, rounds, centroids, assign, ws, stream));
+}
+
+int kvs_medoids(const float* x, int64_t n, int64_t dim, const int32_t* assign, int32_t clusters,
+                int32_t* medoid, float* totals, void* stream) {
+  if (int st = check_embed(n, dim, clusters)) return st;
+  if (!medoid || (n > 0 && (!x || !assign || !totals))) return KVS_E_NULL;
+  if (!aligned(medoid, 4) || (x && !aligned(x, 16)) || (assign && !aligned(assign, 4)) ||
+      (totals && !aligned(totals, 4)))
+    return KVS_E_ALIGN;
+  return to_status(launch_medoids(x, n, dim, assign, clusters, medoid, totals, stream));
+}
+
+int kvs_match_episodes(const float* q, int64_t m, int64_t dim, const float* centroids,
+                       int32_t clusters, int32_t* episode, void* stream) {
+  if (int st = check_embed(m, dim, clusters)) return st;
+  if (m == 0) return KVS_OK;
+  if (!q || !centroids || !episode) return KVS_E_NULL;
+  if (!aligned(q, 16) || !aligned(centroids, 16) || !aligned(episode, 4)) return KVS_E_ALIGN;
+  return to_status(launch_nearest(q, m, dim, centroids, clusters, episode, stream));
+}
+
 int kvs_append_rows(int32_t slabs, int32_t head_dim, int32_t dtype, const void* src,
                     int64_t src_row_stride, int64_t src_row0, int64_t n_rows, void* dst,
                     int64_t dst_row_stride, int64_t dst_row0, void* stream) {

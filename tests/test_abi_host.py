@@ -397,3 +397,28 @@ def test_key_similarity_rejects_bad_arguments(K):
     assert call(n=wb - 1) == 6
     assert call(out=FAKE + 4) == 5
     assert call(b=FAKE + 8) == 5
+
+
+def test_episode_entry_points_reject_bad_arguments(K):
+    h = raw(K)
+    ws = K.kvs_kmeans_workspace_bytes(1000, 1024, 4)
+    assert ws >= 4 * 4 * 1024 * 4 and K.kvs_kmeans_workspace_bytes(10, 6, 4) == 0   # dim % 4
+    assert K.kvs_kmeans_workspace_bytes(10, 4096, 4) == 0 and K.kvs_kmeans_workspace_bytes(10, 8, 17) == 0
+
+    def km(n=1000, dim=1024, e=4, init=FAKE, rounds=3, x=FAKE, w=FAKE, wb=ws):
+        return h.kvs_kmeans(x, n, dim, e, init, rounds, FAKE, FAKE, w, wb, None)
+
+    assert km(dim=1022) == 2
+    assert km(e=0) == 2
+    assert km(rounds=-1) == 2
+    assert km(init=None) == 1
+    assert km(x=None) == 1
+    assert km(w=None) == 1
+    assert km(wb=ws - 1) == 6
+    assert km(x=FAKE + 4) == 5
+    assert h.kvs_medoids(FAKE, 10, 8, FAKE, 2, None, FAKE, None) == 1
+    assert h.kvs_medoids(FAKE, 10, 8, FAKE, 2, FAKE, None, None) == 1
+    assert h.kvs_medoids(FAKE + 8, 10, 8, FAKE, 2, FAKE, FAKE, None) == 5
+    assert h.kvs_match_episodes(FAKE, 10, 8, None, 2, FAKE, None) == 1
+    assert h.kvs_match_episodes(FAKE, 10, 8, FAKE, 20, FAKE, None) == 2
+    assert h.kvs_match_episodes(None, 0, 8, None, 2, None, None) == 0

@@ -1,0 +1,136 @@
+"""GPU episode clustering, medoids and question matching against the oracle
+(EpiCache review, "방법: 3단계" (1) and (3), Fig. 3(a) and (c)).
+
+Assignments are argmins of fp32 squared distances, the oracle's of float64
+ones: they must agree except where the two nearest centroids are within the
+fp32 rounding of the distance (relative 1e-5 here, for sums of <= 2048 terms).
+Centroids: |gpu - oracle| <= 1e-5 in absolute terms (coordinates of unit-norm
+embeddings; fp32 sums of <= 256 points per block, float64 across blocks).
+Medoid totals: relative 1e-5.  Iterations are checked under teacher forcing:
+each GPU round starts from the oracle's centroids of the previous round.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+REL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def K():
+    import kv_cache_compression_kvs_amd as pkg
+    return pkg
+
+
+def d2(x, c):
+    return ((x[:, None, :] - c[None, :, :]) ** 2).sum(-1)
+
+
+def assert_nearest_valid(got, x, c, what=""):
+    """got[i] is the oracle's nearest centroid, or within REL of it."""
+    dist = d2(np.asarray(x, np.float64), np.asarray(c, np.float64))
+    want = np.argmin(dist, 1)
+    bad = []
+    for i in np.nonzero(got != want)[0]:
+        best = dist[i, want[i]]
+        if dist[i, got[i]] - best > REL * max(best, 1e-30):
+            bad.append(i)
+    assert not bad, f"{what}: {len(bad)} assignments are not nearest"
+    return int(np.sum(got != want))
+
+
+def gpu_kmeans(K, x, init, rounds):
+    xd, cd = x.cuda(), init.cuda()
+    cent = torch.empty_like(cd)
+    assign = torch.full((x.shape[0],), -1, dtype=torch.int32, device="cuda")
+    K.kvs_kmeans(xd, cd, rounds, cent, assign)
+    torch.cuda.synchronize()
+    return cent.cpu().double().numpy(), assign.cpu().numpy().astype(np.int64)
+
+
+@pytest.mark.parametrize("n,dim,e", [(1000, 1024, 4), (333, 100, 7), (64, 2048, 16), (5, 4, 1)])
+def test_nearest_matches_oracle(K, n, dim, e):
+    g = torch.Generator().manual_seed(n + dim)
+    x = torch.randn(n, dim, generator=g)
+    c = torch.randn(e, dim, generator=g)
+    out = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    K.kvs_match_episodes(x.cuda(), c.cuda(), out)
+    torch.cuda.synchronize()
+    assert_nearest_valid(out.cpu().numpy(), x.double().numpy(), c.double().numpy(), "nearest")
+
+
+def test_kmeans_recovers_separated_episodes(K):
+    emb = gen.episode_embeddings(1024, 1024, 4, seed=0)
+    x = emb["x"]
+    init = x[emb["init_index"]].contiguous()
+    c, a = gpu_kmeans(K, x, init, 10)
+    oc, oa = O.kmeans(x.double().numpy(), init.double().numpy(), 10)
+    assert np.array_equal(a, oa) and np.array_equal(a, emb["labels"].numpy())
+    assert np.abs(c - oc).max() <= 1e-5
+    # questions go to their topic's episode
+    ep = torch.full((emb["q"].shape[0],), -1, dtype=torch.int32, device="cuda")
+    K.kvs_match_episodes(emb["q"].cuda(), torch.from_numpy(c).float().cuda(), ep)
+    torch.cuda.synchronize()
+    assert np.array_equal(ep.cpu().numpy(), emb["q_labels"].numpy())
+    assert np.array_equal(ep.cpu().numpy(), O.nearest_centroid(emb["q"].double().numpy(), oc))
+
+
+def test_kmeans_rounds_teacher_forced_on_overlapping_data(K):
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(700, 64, generator=g)          # no cluster structure: many near-ties
+    init = x[:5].clone()
+    x64 = x.double().numpy()
+    for r in range(5):
+        cr = O.kmeans(x64, init.double().numpy(), r)[0]
+        crt = torch.from_numpy(cr).float()
+        _, a0 = gpu_kmeans(K, x, crt, 0)
+        assert_nearest_valid(a0, x64, crt.double().numpy(), f"round {r} assignment")
+        c1, a1 = gpu_kmeans(K, x, crt, 1)
+        want = crt.double().numpy().copy()
+        for e in range(5):
+            if np.any(a0 == e):
+                want[e] = x64[a0 == e].mean(0)
+        assert np.abs(c1 - want).max() <= 1e-5, r
+        assert_nearest_valid(a1, x64, c1, f"round {r} final assignment")
+
+
+def test_kmeans_zero_points_and_empty_clusters(K):
+    init = torch.randn(3, 8)
+    cent = torch.empty(3, 8, device="cuda")
+    K.kvs_kmeans(torch.empty(0, 8, device="cuda"), init.cuda(), 4, cent,
+                 torch.empty(0, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(cent.cpu(), init)
+    x = torch.tensor([[0.0] * 4, [0.1] * 4, [10.0] * 4, [10.2] * 4])
+    init = torch.tensor([[0.0] * 4, [10.0] * 4, [1000.0] * 4])
+    c, a = gpu_kmeans(K, x, init, 3)
+    assert a.tolist() == [0, 0, 1, 1] and c[2, 0] == 1000.0
+    assert abs(c[0, 0] - 0.05) < 1e-6 and abs(c[1, 0] - 10.1) < 1e-5
+
+
+@pytest.mark.parametrize("n,dim,e", [(1024, 1024, 4), (257, 2048, 3), (40, 12, 5)])
+def test_medoids_match_oracle(K, n, dim, e):
+    g = torch.Generator().manual_seed(n)
+    x = torch.randn(n, dim, generator=g)
+    a = torch.randint(0, e - 1 if e > 3 else e, (n,), generator=g).int()   # e > 3: one cluster empty
+    totals = torch.full((n,), float("nan"), device="cuda")
+    med = torch.full((e,), -9, dtype=torch.int32, device="cuda")
+    K.kvs_medoids(x.cuda(), a.cuda(), e, med, totals)
+    torch.cuda.synchronize()
+    x64, a64 = x.double().numpy(), a.numpy().astype(np.int64)
+    want_t = O.medoid_totals(x64, a64)
+    got_t = totals.cpu().double().numpy()
+    assert np.all(np.abs(got_t - want_t) <= REL * want_t + 1e-6)
+    want = O.medoids(x64, a64, e)
+    got = med.cpu().numpy()
+    for c in range(e):
+        if want[c] < 0:
+            assert got[c] == -1
+            continue
+        assert a64[got[c]] == c
+        best = want_t[want[c]]
+        assert want_t[got[c]] - best <= REL * best, (c, got[c], want[c])

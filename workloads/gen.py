@@ -338,6 +338,34 @@ def calibration_keys(shape: ScoreShape, n_tokens: int, seed: int = 0, device="cp
 
 
 # --------------------------------------------------------------------------
+# episode clustering: segment and question embeddings
+# --------------------------------------------------------------------------
+
+def episode_embeddings(n_segments: int, dim: int, episodes: int, seed: int = 0,
+                       n_questions: int = 64, noise: float = 0.9) -> Dict[str, torch.Tensor]:
+    """Unit-norm fp32 segment embeddings [n_segments, dim] of a conversation
+    that drifts between `episodes` topics in runs of 2-12 segments, questions
+    [n_questions, dim] about seeded topics, the true labels of both, and the
+    initial centroids' row indices (the first segment of each topic's first
+    run, so every cluster starts inside its topic)."""
+    g = _gen("cpu", seed, "episodes", n_segments, dim, episodes)
+    topics = _unit(torch.randn(episodes, dim, generator=g)) * math.sqrt(dim) / 8
+    labels = torch.empty(n_segments, dtype=torch.int64)
+    i = 0
+    while i < n_segments:
+        run = int(torch.randint(2, 13, (1,), generator=g))
+        labels[i:i + run] = int(torch.randint(0, episodes, (1,), generator=g))
+        i += run
+    labels[:episodes] = torch.arange(episodes)     # every topic appears early
+    x = _unit(topics[labels] + noise * torch.randn(n_segments, dim, generator=g) / 8)
+    qlab = torch.randint(0, episodes, (n_questions,), generator=g)
+    q = _unit(topics[qlab] + noise * torch.randn(n_questions, dim, generator=g) / 8)
+    init = torch.tensor([int(torch.nonzero(labels == e)[0]) for e in range(episodes)])
+    return {"x": x.float().contiguous(), "labels": labels, "q": q.float().contiguous(),
+            "q_labels": qlab, "init_index": init}
+
+
+# --------------------------------------------------------------------------
 # inputs for the selection and compaction kernels in isolation
 # --------------------------------------------------------------------------
 
