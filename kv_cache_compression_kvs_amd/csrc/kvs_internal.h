@@ -86,7 +86,7 @@ int launch_append(int32_t slabs, int64_t row_bytes, const void* src, int64_t src
 // Multi-workgroup radix select: candidates per workgroup, the largest
 // per-unit candidate count the single-workgroup select handles, and the
 // workspace it carves (per-unit mode for long caches, and the global mode).
-constexpr int64_t kSelSpan = 16384;
+constexpr int64_t kSelSpan = 4096;
 constexpr int64_t kSelSingleMax = 32 * 1024;
 
 inline bool select_uses_multi(const kvs_problem& p) {
@@ -94,7 +94,8 @@ inline bool select_uses_multi(const kvs_problem& p) {
 }
 
 struct SelectWs {
-  size_t off_hist = 0, off_state = 0, off_cnt = 0, off_before = 0, off_ekeep = 0, bytes = 0;
+  size_t off_hist = 0, off_state = 0, off_cnt = 0, off_before = 0, off_ekeep = 0, off_tot = 0;
+  size_t bytes = 0;
 };
 
 inline SelectWs select_ws_layout(const kvs_problem& p) {
@@ -105,7 +106,7 @@ inline SelectWs select_ws_layout(const kvs_problem& p) {
   SelectWs w;
   size_t off = 0;
   w.off_hist = off;
-  off += r256(units * 256 * 4);
+  off += r256(units * 8 * 256 * 4);  // one 256-bin histogram per XCD and segment
   w.off_state = off;
   off += r256(units * 16);
   w.off_cnt = off;
@@ -114,6 +115,8 @@ inline SelectWs select_ws_layout(const kvs_problem& p) {
   off += r256(units * (nch ? nch : 1) * 8);
   w.off_ekeep = off;
   off += r256(units * 4);
+  w.off_tot = off;
+  off += r256(units * 8);
   w.bytes = off;
   return w;
 }

@@ -51,8 +51,11 @@ struct SelArgs {
   LayerTable t;
 };
 
-// Inclusive scan over the 1024 threads; returns the block total in *total.
+// Inclusive scan over the NT threads of the workgroup (wsum holds 2 * NT / 64
+// words); returns the block total in *total.
+template <int NT = kThreads>
 __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t* wsum, uint32_t* total) {
+  constexpr int kWaves = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -310,7 +313,9 @@ __global__ __launch_bounds__(kThreads) void query_select_kernel(QueryArgs a) {
 //
 // A segment is the candidate set one threshold is found for: one unit's
 // positions [S, N), or (global) every unit's, in (unit, position) order.  Its
-// candidates are cut into spans of kSpan, one workgroup per (span, unit):
+// candidates are cut into spans of kSpan, one 256-thread workgroup per (span,
+// unit) (small workgroups keep many resident per CU, so one's load latency
+// hides behind another's counting):
 //   init       per segment: histogram cleared, (prefix, rem) = (0, need)
 //   hist, pick four 8-bit digits, most significant first: each span counts
 //              the candidates that match the prefix so far into per-wave LDS
@@ -321,26 +326,34 @@ __global__ __launch_bounds__(kThreads) void query_select_kernel(QueryArgs a) {
 //              tau, the key of the need-th best candidate, and rem is e, the
 //              number of candidates equal to tau that are kept.
 //   count      per span: candidates above tau and equal to tau
-//   scan       per unit: exclusive prefix counts of its spans; in global mode
-//              also each unit's share of the e tied candidates (lower units
-//              first, as the order (score desc, unit, position) says), its
-//              kept count and the start of its list
+//   scan       per unit (one wave): exclusive prefix counts of its spans; in
+//              global mode then one workgroup gives each unit its share of the
+//              e tied candidates (lower units first, as the order (score
+//              desc, unit, position) says), its kept count and the start of
+//              its list
 //   emit       per span: keys staged in LDS by coalesced loads, then an
 //              ordered block scan over kItems consecutive keys per thread places
 //              every kept candidate at its rank in the unit's ascending list
 // Only integer atomics are used, so the result does not depend on scheduling.
-constexpr int kSpan = kSelSpan;  // candidates per workgroup
-static_assert(kSpan == kThreads * kItems, "one span is kItems candidates per thread");
+constexpr int kMT = 256;          // threads per span workgroup
+constexpr int kMW = kMT / 64;
+constexpr int kSpan = kSelSpan;   // candidates per span workgroup
+static_assert(kSpan == kMT * kItems, "one span is kItems candidates per thread");
+// Each segment's histogram has one copy per XCD (workgroups are dispatched
+// round-robin over the 8 XCDs), so the spans of a large segment do not all
+// queue on the same 256 counters; the pick sums the copies.
+constexpr int kCopies = 8;
 
 struct MultiArgs {
   const float* scores;
   int32_t* kept;
   int64_t* offsets;   // global mode: [units + 1], start of each unit's list
-  uint32_t* hist;     // [segments][256]
+  uint32_t* hist;     // [segments][kCopies][256]: one copy per XCD
   uint32_t* state;    // [segments][4]: prefix, rem, done, -
   uint32_t* cnt;      // [units][nch][2]: (above tau, equal to tau) of each span
   uint32_t* before;   // [units][nch][2]: the same, summed over the unit's earlier spans
   uint32_t* ekeep;    // global mode: [units], tau-equal candidates each unit keeps
+  uint32_t* tot;      // global mode: [units][2], (above tau, equal to tau) of each unit
   int64_t N, S;       // S is min(n_sinks, N)
   int64_t nc;         // N - S candidates per unit
   int64_t need;       // global mode: non-sink entries kept over all units
@@ -353,7 +366,7 @@ __device__ __forceinline__ int64_t segment_need(const MultiArgs& a, int64_t seg)
 }
 
 // Keys of the kItems candidates a thread owns in an order-free pass over a
-// span of len >= 1 candidates at p: candidate j * 4 * kThreads + 4 * tid + q is
+// span of len >= 1 candidates at p: candidate j * 4 * kMT + 4 * tid + q is
 // item 4j + q (idx), so every load instruction of a wave covers 1 KiB.  VEC:
 // p is 16-byte aligned and len a multiple of 4, so each group of four is one
 // 16-byte load.  Loads are clamped into the span; items with idx >= len are
@@ -363,7 +376,7 @@ __device__ __forceinline__ void keys_strided(const float* p, int64_t len, int ti
                                              uint32_t (&x)[kItems], int64_t (&idx)[kItems]) {
 #pragma unroll
   for (int j = 0; j < kItems / 4; ++j) {
-    const int64_t b = (int64_t)j * 4 * kThreads + 4 * tid;
+    const int64_t b = (int64_t)j * 4 * kMT + 4 * tid;
     if (VEC) {
       const float4 v = *reinterpret_cast<const float4*>(p + min(b, len - 4));
       x[4 * j + 0] = order_key(v.x);
@@ -381,7 +394,8 @@ __device__ __forceinline__ void keys_strided(const float* p, int64_t len, int ti
 
 __global__ __launch_bounds__(256) void ms_init(MultiArgs a) {
   const int64_t seg = blockIdx.x;
-  a.hist[seg * 256 + threadIdx.x] = 0u;
+#pragma unroll
+  for (int c = 0; c < kCopies; ++c) a.hist[(seg * kCopies + c) * 256 + threadIdx.x] = 0u;
   if (threadIdx.x == 0) {
     const int64_t count = a.global ? a.nc * a.units : a.nc;
     const int64_t need = segment_need(a, seg);
@@ -404,8 +418,8 @@ __global__ __launch_bounds__(256) void ms_init(MultiArgs a) {
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void ms_hist(MultiArgs a, int shift) {
-  __shared__ uint32_t hw[kWaves * 256];
+__global__ __launch_bounds__(kMT) void ms_hist(MultiArgs a, int shift) {
+  __shared__ uint32_t hw[kMW * 256];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t u = blockIdx.y;
   const int64_t seg = a.global ? 0 : u;
@@ -413,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void ms_hist(MultiArgs a, int shift) {
   if (st[2]) return;  // the same for the whole workgroup
   const uint32_t prefix = st[0];
   const uint32_t mask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-  for (int b = tid; b < kWaves * 256; b += kThreads) hw[b] = 0u;
+  for (int b = tid; b < kMW * 256; b += kMT) hw[b] = 0u;
   const int64_t c0 = (int64_t)blockIdx.x * kSpan;
   const int64_t len = min((int64_t)kSpan, a.nc - c0);
   uint32_t x[kItems];
@@ -429,8 +443,9 @@ __global__ __launch_bounds__(kThreads) void ms_hist(MultiArgs a, int shift) {
   if (tid < 256) {
     uint32_t c = 0u;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) c += hw[w * 256 + tid];
-    if (c) atomicAdd(&a.hist[seg * 256 + tid], c);
+    for (int w = 0; w < kMW; ++w) c += hw[w * 256 + tid];
+    const int64_t copy = (blockIdx.x + (int64_t)blockIdx.y * gridDim.x) % kCopies;
+    if (c) atomicAdd(&a.hist[(seg * kCopies + copy) * 256 + tid], c);
   }
 }
 
@@ -444,9 +459,12 @@ __global__ __launch_bounds__(kThreads) void ms_pick(MultiArgs a, int shift) {
   const uint32_t rem = st[1];
   uint32_t c = 0u;
   if (tid < 256) {  // thread t holds bin 255 - t: the scan runs from the top bin down
-    uint32_t* h = a.hist + seg * 256 + 255 - tid;
-    c = *h;
-    *h = 0u;        // cleared for the next digit
+#pragma unroll
+    for (int k = 0; k < kCopies; ++k) {
+      uint32_t* h = a.hist + (seg * kCopies + k) * 256 + 255 - tid;
+      c += *h;
+      *h = 0u;      // cleared for the next digit
+    }
   }
   uint32_t tot;
   const uint32_t cum = block_scan(c, wsum, &tot);
@@ -458,8 +476,8 @@ __global__ __launch_bounds__(kThreads) void ms_pick(MultiArgs a, int shift) {
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void ms_count(MultiArgs a) {
-  __shared__ uint32_t wsum[2 * kWaves];
+__global__ __launch_bounds__(kMT) void ms_count(MultiArgs a) {
+  __shared__ uint32_t wsum[2 * kMW];
   const int tid = threadIdx.x;
   const int64_t u = blockIdx.y;
   const uint32_t tau = a.state[(a.global ? 0 : u) * 4];
@@ -475,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void ms_count(MultiArgs a) {
     neq += idx[j] < len && x[j] == tau;
   }
   uint32_t tot;
-  block_scan((ngt << 16) | neq, wsum, &tot);  // a span's counts fit 16 bits each
+  block_scan<kMT>((ngt << 16) | neq, wsum, &tot);  // a span's counts fit 16 bits each
   if (tid == 0) {
     uint32_t* c = a.cnt + (u * a.nch + blockIdx.x) * 2;
     c[0] = tot >> 16;
@@ -483,21 +501,43 @@ __global__ __launch_bounds__(kThreads) void ms_count(MultiArgs a) {
   }
 }
 
-// Per-unit mode: one thread per unit.
-__global__ __launch_bounds__(256) void ms_scan_units(MultiArgs a) {
-  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (u >= a.units) return;
-  uint32_t gb = 0u, eb = 0u;
-  for (int64_t c = 0; c < a.nch; ++c) {
+// One wave per unit: exclusive prefix counts of the unit's spans (64 spans
+// per step, carried), and in global mode the unit's totals.
+__global__ __launch_bounds__(64) void ms_scan_units(MultiArgs a) {
+  const int64_t u = blockIdx.x;
+  const int lane = threadIdx.x;
+  uint32_t cgt = 0u, ceq = 0u;
+  for (int64_t c0 = 0; c0 < a.nch; c0 += 64) {
+    const int64_t c = c0 + lane;
     const int64_t o = (u * a.nch + c) * 2;
-    a.before[o] = gb;
-    a.before[o + 1] = eb;
-    gb += a.cnt[o];
-    eb += a.cnt[o + 1];
+    const uint32_t g = c < a.nch ? a.cnt[o] : 0u;
+    const uint32_t e = c < a.nch ? a.cnt[o + 1] : 0u;
+    uint32_t ig = g, ie = e;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t yg = __shfl_up(ig, off, 64);
+      const uint32_t ye = __shfl_up(ie, off, 64);
+      if (lane >= off) {
+        ig += yg;
+        ie += ye;
+      }
+    }
+    if (c < a.nch) {
+      a.before[o] = cgt + ig - g;
+      a.before[o + 1] = ceq + ie - e;
+    }
+    cgt += __shfl(ig, 63, 64);
+    ceq += __shfl(ie, 63, 64);
+  }
+  if (a.global && lane == 0) {
+    a.tot[u * 2] = cgt;
+    a.tot[u * 2 + 1] = ceq;
   }
 }
 
-// Global mode: one workgroup walks the units in order.
+// Global mode: one workgroup walks the unit totals in order, giving each
+// unit its share e_u of the tied candidates (lower units first), its kept
+// count and the start of its list.
 __global__ __launch_bounds__(kThreads) void ms_scan_global(MultiArgs a) {
   __shared__ uint32_t wsum[2 * kWaves];
   const int tid = threadIdx.x;
@@ -505,16 +545,8 @@ __global__ __launch_bounds__(kThreads) void ms_scan_global(MultiArgs a) {
   uint64_t carry_eq = 0, carry_k = 0;
   for (int64_t base = 0; base < a.units; base += kThreads) {
     const int64_t u = base + tid;
-    uint32_t gt_u = 0u, eq_u = 0u;
-    if (u < a.units) {
-      for (int64_t c = 0; c < a.nch; ++c) {
-        const int64_t o = (u * a.nch + c) * 2;
-        a.before[o] = gt_u;
-        a.before[o + 1] = eq_u;
-        gt_u += a.cnt[o];
-        eq_u += a.cnt[o + 1];
-      }
-    }
+    const uint32_t gt_u = u < a.units ? a.tot[u * 2] : 0u;
+    const uint32_t eq_u = u < a.units ? a.tot[u * 2 + 1] : 0u;
     uint32_t tot_eq;
     const uint32_t inc_eq = block_scan(eq_u, wsum, &tot_eq);
     const uint64_t eq_before = carry_eq + (inc_eq - eq_u);
@@ -533,8 +565,8 @@ __global__ __launch_bounds__(kThreads) void ms_scan_global(MultiArgs a) {
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void ms_emit(MultiArgs a) {
-  __shared__ uint32_t wsum[2 * kWaves];
+__global__ __launch_bounds__(kMT) void ms_emit(MultiArgs a) {
+  __shared__ uint32_t wsum[2 * kMW];
   __shared__ uint32_t staged[kSpan];
   const int tid = threadIdx.x;
   const int64_t u = blockIdx.y, c = blockIdx.x;
@@ -554,7 +586,7 @@ __global__ __launch_bounds__(kThreads) void ms_emit(MultiArgs a) {
     need_u = kl - a.S;
   }
   if (c == 0)
-    for (int64_t i = tid; i < a.S; i += kThreads) out[i] = (int32_t)i;
+    for (int64_t i = tid; i < a.S; i += kMT) out[i] = (int32_t)i;
   const int64_t c0 = c * kSpan;
   const int64_t len = min((int64_t)kSpan, a.nc - c0);
   if (len <= 0) return;  // no candidate at all (N <= S): only the sinks
@@ -579,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void ms_emit(MultiArgs a) {
   }
   const uint32_t packed = (ngt << 16) | neq;
   uint32_t tot;
-  const uint32_t excl = block_scan(packed, wsum, &tot) - packed;
+  const uint32_t excl = block_scan<kMT>(packed, wsum, &tot) - packed;
   const uint32_t* bf = a.before + (u * a.nch + c) * 2;
   uint64_t gt_before = bf[0] + (excl >> 16);
   uint64_t eq_before = bf[1] + (excl & 0xFFFFu);
@@ -613,24 +645,22 @@ int multi_select(MultiArgs a, int64_t segments, hipStream_t st) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       {
         TraceScope ts("select_hist", st);
-        hipLaunchKernelGGL(ms_hist<VEC>, spans, dim3(kThreads), 0, st, a, shift);
+        hipLaunchKernelGGL(ms_hist<VEC>, spans, dim3(kMT), 0, st, a, shift);
       }
       TraceScope ts("select_pick", st);
       hipLaunchKernelGGL(ms_pick, dim3((unsigned)segments), dim3(kThreads), 0, st, a, shift);
     }
     TraceScope ts("select_count", st);
-    hipLaunchKernelGGL(ms_count<VEC>, spans, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(ms_count<VEC>, spans, dim3(kMT), 0, st, a);
   }
   {
     TraceScope ts("select_scan", st);
-    if (a.global)
-      hipLaunchKernelGGL(ms_scan_global, dim3(1), dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL(ms_scan_units, dim3((unsigned)ceil_div(a.units, 256)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(ms_scan_units, dim3((unsigned)a.units), dim3(64), 0, st, a);
+    if (a.global) hipLaunchKernelGGL(ms_scan_global, dim3(1), dim3(kThreads), 0, st, a);
   }
   TraceScope ts("select_emit", st);
   hipLaunchKernelGGL(ms_emit<VEC>, dim3((unsigned)std::max<int64_t>(a.nch, 1), (unsigned)a.units),
-                     dim3(kThreads), 0, st, a);
+                     dim3(kMT), 0, st, a);
   return (int)hipGetLastError();
 }
 
@@ -660,6 +690,7 @@ int run_multi(const kvs_problem& p, const float* scores, const LayerTable* t, in
   a.cnt = reinterpret_cast<uint32_t*>(base + w.off_cnt);
   a.before = reinterpret_cast<uint32_t*>(base + w.off_before);
   a.ekeep = reinterpret_cast<uint32_t*>(base + w.off_ekeep);
+  a.tot = reinterpret_cast<uint32_t*>(base + w.off_tot);
   const int64_t segments = t ? units : 1;
   const bool vec = (N % 4 == 0) && (S % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
   return vec ? multi_select<true>(a, segments, st) : multi_select<false>(a, segments, st);
