@@ -361,6 +361,9 @@ int kvs_sensitivity(int32_t layers, const double* similarity, double* sens);
  *   points of its cluster (device fp32 [n] out); medoid[e] = the member of
  *   cluster e with the least total, ties to the lower index, -1 if empty
  *   (device int32 [clusters] out).  assign: device int32 [n] in [0, clusters).
+ *   n <= 64 * 65535.  ws: device workspace of kvs_medoids_workspace_bytes(n,
+ *   dim, clusters) bytes (about n * n / 16 bytes: one partial sum per point
+ *   and 64-point tile), 256-byte aligned.
  * kvs_match_episodes: episode[j] = the centroid nearest to query row j (as in
  *   the assignment), q: device [m, dim], episode: device int32 [m].
  * Errors: KVS_E_SHAPE (sizes above), KVS_E_NULL, KVS_E_ALIGN (rows 16-byte,
@@ -370,8 +373,9 @@ size_t kvs_kmeans_workspace_bytes(int64_t n, int64_t dim, int32_t clusters);
 int kvs_kmeans(const float* x, int64_t n, int64_t dim, int32_t clusters, const float* init,
                int32_t rounds, float* centroids, int32_t* assign, void* ws, size_t ws_bytes,
                void* stream);
+size_t kvs_medoids_workspace_bytes(int64_t n, int64_t dim, int32_t clusters);
 int kvs_medoids(const float* x, int64_t n, int64_t dim, const int32_t* assign, int32_t clusters,
-                int32_t* medoid, float* totals, void* stream);
+                int32_t* medoid, float* totals, void* ws, size_t ws_bytes, void* stream);
 int kvs_match_episodes(const float* q, int64_t m, int64_t dim, const float* centroids,
                        int32_t clusters, int32_t* episode, void* stream);
 

@@ -9,7 +9,7 @@ from .api import (KvsError, kvs_append_rows, kvs_check_problem, kvs_compact,  # 
                   kvs_compact_ragged, kvs_compress_block, kvs_compress_block_seg,
                   kvs_compress_global, kvs_decode_ragged, kvs_decode_workspace_bytes,
                   kvs_key_similarity, kvs_kmeans, kvs_kmeans_workspace_bytes,
-                  kvs_layer_budgets, kvs_match_episodes, kvs_medoids, kvs_select_global,
+                  kvs_layer_budgets, kvs_match_episodes, kvs_medoids, kvs_medoids_workspace_bytes, kvs_select_global,
                   kvs_sensitivity, kvs_similarity_workspace_bytes,
                   kvs_num_chunks, kvs_num_queries, kvs_query_counts, kvs_query_select,
                   kvs_query_workspace_bytes, kvs_score, kvs_select, kvs_status_string,

@@ -93,8 +93,9 @@ SIGNATURES = {
     "kvs_kmeans_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int32]),
     "kvs_kmeans": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_int32, c_void_p,
                              c_void_p, c_void_p, c_size_t, c_void_p]),
+    "kvs_medoids_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int32]),
     "kvs_medoids": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_void_p,
-                              c_void_p]),
+                              c_void_p, c_size_t, c_void_p]),
     "kvs_match_episodes": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_int32, c_void_p,
                                      c_void_p]),
     "kvs_append_rows": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_int64, c_int64,

@@ -313,12 +313,22 @@ def kvs_kmeans(x: Tensorish, init: Tensorish, rounds: int, centroids: Tensorish,
                                  _dev(ws, "ws"), ws_bytes, _stream(stream)), "kvs_kmeans")
 
 
+def kvs_medoids_workspace_bytes(n: int, dim: int, clusters: int) -> int:
+    return int(_lib.lib().kvs_medoids_workspace_bytes(n, dim, clusters))
+
+
 def kvs_medoids(x: Tensorish, assign: Tensorish, clusters: int, medoid: Tensorish,
-                totals: Tensorish, stream=None) -> None:
+                totals: Tensorish, ws: Tensorish = None, ws_bytes: Optional[int] = None,
+                stream=None) -> None:
     n, dim = x.shape
+    if ws is None:
+        ws = torch.empty(max(kvs_medoids_workspace_bytes(n, dim, clusters), 256),
+                         dtype=torch.uint8, device=x.device)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
     _check(_lib.lib().kvs_medoids(_dev(x, "x"), n, dim, _dev(assign, "assign"), clusters,
-                                  _dev(medoid, "medoid"), _dev(totals, "totals"),
-                                  _stream(stream)), "kvs_medoids")
+                                  _dev(medoid, "medoid"), _dev(totals, "totals"), _dev(ws, "ws"),
+                                  ws_bytes, _stream(stream)), "kvs_medoids")
 
 
 def kvs_match_episodes(q: Tensorish, centroids: Tensorish, episode: Tensorish,

@@ -16,10 +16,10 @@
 //   centroid_final   per (cluster, dimension): the blocks' partials in a fixed
 //                    order in float64, divided by the member count; an empty
 //                    cluster keeps its centroid.
-//   medoid_total     for 8 candidate points (rows staged in LDS) at a time,
-//                    every thread walks its share of all points and adds the
-//                    Euclidean distance of those in the candidate's cluster;
-//                    a fixed-order tree sums the threads.
+//   medoid_tile      pairwise distances in 64 x 64 tiles (4 x 4 pairs per
+//                    thread, 32-dimension chunks staged in LDS), summed per row
+//                    over the pairs that share a cluster; medoid_sum adds the
+//                    tiles' row sums in a fixed order.
 //   medoid_pick      per cluster, the member with the least total, ties to
 //                    the lower index (-1 if the cluster is empty).
 #include <cmath>
@@ -33,9 +33,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBlockPoints = 256;  // points per centroid_partial workgroup
+constexpr int kBlockPoints = 32;   // points per centroid_partial workgroup
 constexpr int kSliceDims = 1024;   // dimensions per centroid_partial workgroup
-constexpr int kCand = 8;           // candidate points per medoid_total workgroup
 
 __global__ __launch_bounds__(kThreads) void nearest_kernel(const float* __restrict__ x, int64_t n,
                                                            int64_t D, const float* __restrict__ c,
@@ -136,62 +135,99 @@ __global__ __launch_bounds__(kThreads) void copy_f32(const float* __restrict__ s
   if (i < n) dst[i] = src[i];
 }
 
-__global__ __launch_bounds__(kThreads) void medoid_total(const float* __restrict__ x, int64_t n,
-                                                         int64_t D,
-                                                         const int32_t* __restrict__ assign,
-                                                         float* __restrict__ total) {
-  __shared__ float cand[kCand * kMaxEmbedDim];  // [kCand][D]
-  __shared__ float red[kThreads][kCand];
-  const int tid = threadIdx.x;
-  const int64_t i0 = (int64_t)blockIdx.x * kCand;
-  int32_t ca[kCand];
+// Pairwise distances in 64 x 64 tiles: thread (ty, tx) of the 16 x 16 grid owns
+// the 4 x 4 pairs (i0 + 4 ty + r, j0 + 4 tx + c); the two row sets stream through
+// LDS in chunks of 32 dimensions (stored transposed, so the inner loop reads
+// four consecutive rows of one dimension as one 16-byte word).  Each pair adds
+// its Euclidean distance to row i's sum if i and j share a cluster; a row's sum
+// over the tile goes to part[j tile][i].
+constexpr int kTile = 64;
+constexpr int kChunk = 32;
+
+__global__ __launch_bounds__(kThreads) void medoid_tile(const float* __restrict__ x, int64_t n,
+                                                        int64_t D,
+                                                        const int32_t* __restrict__ assign,
+                                                        float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) float xi[kChunk][kTile];
+  __shared__ __attribute__((aligned(16))) float xj[kChunk][kTile];
+  __shared__ float rsum[16][kTile];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int64_t i0 = (int64_t)blockIdx.x * kTile, j0 = (int64_t)blockIdx.y * kTile;
+  float acc[4][4];
 #pragma unroll
-  for (int c = 0; c < kCand; ++c) {
-    const int64_t i = min(i0 + c, n - 1);
-    ca[c] = i0 + c < n ? assign[i] : -1;
-    for (int64_t k = tid; k < D; k += kThreads) cand[c * D + k] = x[i * D + k];
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
   }
-  __syncthreads();
-  float acc[kCand];
+  // loader: thread t copies rows (t / 8) and (t / 8) + 32, dimensions
+  // 4 * (t % 8) .. +3 of the chunk, for both row sets
+  const int lr = tid >> 3, ld = (tid & 7) * 4;
+  for (int64_t k0 = 0; k0 < D; k0 += kChunk) {
 #pragma unroll
-  for (int c = 0; c < kCand; ++c) acc[c] = 0.f;
-  for (int64_t j = tid; j < n; j += kThreads) {
-    const int32_t aj = assign[j];
-    bool any = false;
-#pragma unroll
-    for (int c = 0; c < kCand; ++c) any |= ca[c] == aj;
-    if (!any) continue;
-    float d2[kCand];
-#pragma unroll
-    for (int c = 0; c < kCand; ++c) d2[c] = 0.f;
-    const float* xr = x + j * D;
-    for (int64_t k = 0; k < D; k += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(xr + k);
-#pragma unroll
-      for (int c = 0; c < kCand; ++c) {
-        const float* cr = cand + c * D + k;  // the same address on every lane: broadcast
-        const float e0 = v.x - cr[0], e1 = v.y - cr[1], e2 = v.z - cr[2], e3 = v.w - cr[3];
-        d2[c] = fmaf(e0, e0, d2[c]);
-        d2[c] = fmaf(e1, e1, d2[c]);
-        d2[c] = fmaf(e2, e2, d2[c]);
-        d2[c] = fmaf(e3, e3, d2[c]);
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int row = lr + 32 * h;
+      const int64_t gi = min(i0 + row, n - 1), gj = min(j0 + row, n - 1);
+      const bool in_d = k0 + ld < D;  // D is a multiple of 4
+      float4 a = in_d ? *reinterpret_cast<const float4*>(x + gi * D + k0 + ld) : float4{0, 0, 0, 0};
+      float4 b = in_d ? *reinterpret_cast<const float4*>(x + gj * D + k0 + ld) : float4{0, 0, 0, 0};
+      xi[ld + 0][row] = a.x;
+      xi[ld + 1][row] = a.y;
+      xi[ld + 2][row] = a.z;
+      xi[ld + 3][row] = a.w;
+      xj[ld + 0][row] = b.x;
+      xj[ld + 1][row] = b.y;
+      xj[ld + 2][row] = b.z;
+      xj[ld + 3][row] = b.w;
     }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < kChunk; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(&xi[k][ty * 4]);
+      const float4 b = *reinterpret_cast<const float4*>(&xj[k][tx * 4]);
+      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int c = 0; c < kCand; ++c)
-      if (ca[c] == aj) acc[c] += sqrtf(d2[c]);
-  }
+      for (int r = 0; r < 4; ++r) {
 #pragma unroll
-  for (int c = 0; c < kCand; ++c) red[tid][c] = acc[c];
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) {
-#pragma unroll
-      for (int c = 0; c < kCand; ++c) red[tid][c] += red[tid + s][c];
+        for (int c = 0; c < 4; ++c) {
+          const float d = av[r] - bv[c];
+          acc[r][c] = fmaf(d, d, acc[r][c]);
+        }
+      }
     }
     __syncthreads();
   }
-  if (tid < kCand && i0 + tid < n) total[i0 + tid] = red[0][tid];
+  int32_t ai[4], aj[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t i = i0 + ty * 4 + r, j = j0 + tx * 4 + r;
+    ai[r] = i < n ? assign[i] : -1;
+    aj[r] = j < n ? assign[j] : -2;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float t = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (ai[r] == aj[c]) t += sqrtf(acc[r][c]);
+    rsum[tx][ty * 4 + r] = t;
+  }
+  __syncthreads();
+  if (tid < kTile) {
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) t += rsum[q][tid];
+    if (i0 + tid < n) part[(int64_t)blockIdx.y * n + i0 + tid] = t;
+  }
+}
+
+// total[i] = sum over the j tiles of part[jt][i], in tile order.
+__global__ __launch_bounds__(kThreads) void medoid_sum(const float* __restrict__ part, int64_t n,
+                                                       int64_t jtiles, float* __restrict__ total) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  float t = 0.f;
+  for (int64_t jt = 0; jt < jtiles; ++jt) t += part[jt * n + i];
+  total[i] = t;
 }
 
 __global__ __launch_bounds__(kThreads) void medoid_pick(const int32_t* __restrict__ assign,
@@ -278,17 +314,28 @@ int launch_kmeans(const float* x, int64_t n, int64_t dim, int32_t clusters, cons
 }
 
 int launch_medoids(const float* x, int64_t n, int64_t dim, const int32_t* assign, int32_t clusters,
-                   int32_t* medoid, float* totals, void* stream) {
+                   int32_t* medoid, float* totals, void* ws, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (n > 0) {
-    TraceScope ts("medoid_total", st);
-    hipLaunchKernelGGL(medoid_total, dim3((unsigned)ceil_div(n, kCand)), dim3(kThreads), 0, st,
-                       x, n, dim, assign, totals);
+    const int64_t tiles = ceil_div(n, kTile);
+    float* part = static_cast<float*>(ws);
+    {
+      TraceScope ts("medoid_tile", st);
+      hipLaunchKernelGGL(medoid_tile, dim3((unsigned)tiles, (unsigned)tiles), dim3(kThreads), 0, st,
+                         x, n, dim, assign, part);
+    }
+    TraceScope ts("medoid_sum", st);
+    hipLaunchKernelGGL(medoid_sum, dim3((unsigned)ceil_div(n, kThreads)), dim3(kThreads), 0, st,
+                       part, n, tiles, totals);
   }
   TraceScope ts("medoid_pick", st);
   hipLaunchKernelGGL(medoid_pick, dim3(1), dim3(kThreads), 0, st, assign, totals, n, clusters,
                      medoid);
   return (int)hipGetLastError();
+}
+
+size_t medoid_ws_bytes(int64_t n) {
+  return ((size_t)sizeof(float) * (size_t)(ceil_div(n, kTile) * n) + 255) & ~size_t(255);
 }
 
 }  // namespace kvs

@@ -580,14 +580,21 @@ int kvs_kmeans(const float* x, int64_t n, int64_t dim, int32_t clusters, const f
   return to_status(launch_kmeans(x, n, dim, clusters, init, rounds, centroids, assign, ws, stream));
 }
 
+size_t kvs_medoids_workspace_bytes(int64_t n, int64_t dim, int32_t clusters) {
+  if (check_embed(n, dim, clusters) || n > kMaxMedoidPoints) return 0;
+  return std::max<size_t>(medoid_ws_bytes(n), 256);
+}
+
 int kvs_medoids(const float* x, int64_t n, int64_t dim, const int32_t* assign, int32_t clusters,
-                int32_t* medoid, float* totals, void* stream) {
+                int32_t* medoid, float* totals, void* ws, size_t ws_bytes, void* stream) {
   if (int st = check_embed(n, dim, clusters)) return st;
-  if (!medoid || (n > 0 && (!x || !assign || !totals))) return KVS_E_NULL;
+  if (n > kMaxMedoidPoints) return KVS_E_SHAPE;
+  if (!medoid || (n > 0 && (!x || !assign || !totals || !ws))) return KVS_E_NULL;
+  if (n > 0 && ws_bytes < medoid_ws_bytes(n)) return KVS_E_WORKSPACE;
   if (!aligned(medoid, 4) || (x && !aligned(x, 16)) || (assign && !aligned(assign, 4)) ||
-      (totals && !aligned(totals, 4)))
+      (totals && !aligned(totals, 4)) || (ws && !aligned(ws, 256)))
     return KVS_E_ALIGN;
-  return to_status(launch_medoids(x, n, dim, assign, clusters, medoid, totals, stream));
+  return to_status(launch_medoids(x, n, dim, assign, clusters, medoid, totals, ws, stream));
 }
 
 int kvs_match_episodes(const float* q, int64_t m, int64_t dim, const float* centroids,

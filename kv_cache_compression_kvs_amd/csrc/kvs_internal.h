@@ -77,8 +77,9 @@ int launch_nearest(const float* x, int64_t n, int64_t dim, const float* centroid
                    int32_t clusters, int32_t* out, void* stream);
 int launch_kmeans(const float* x, int64_t n, int64_t dim, int32_t clusters, const float* init,
                   int32_t rounds, float* centroids, int32_t* assign, void* ws, void* stream);
+size_t medoid_ws_bytes(int64_t n);
 int launch_medoids(const float* x, int64_t n, int64_t dim, const int32_t* assign, int32_t clusters,
-                   int32_t* medoid, float* totals, void* stream);
+                   int32_t* medoid, float* totals, void* ws, void* stream);
 int launch_append(int32_t slabs, int64_t row_bytes, const void* src, int64_t src_stride,
                   int64_t src_row0, int64_t n_rows, void* dst, int64_t dst_stride,
                   int64_t dst_row0, void* stream);
@@ -140,6 +141,7 @@ constexpr int64_t kSimRows = 1024;
 // Episode clustering limits: clusters per K-means and embedding width.
 constexpr int kMaxClusters = 16;
 constexpr int64_t kMaxEmbedDim = 2048;
+constexpr int64_t kMaxMedoidPoints = 64 * 65535;  // 64-point tiles, grid y below 2^16
 
 // Pass-1 tiling constants shared by the planner and the kernels.
 constexpr int kP1Rows = 256;      // query rows per pass-1 workgroup (4 waves x 64)
