@@ -16,7 +16,7 @@
 //   decode_prefix  sp[u] = splits before unit u (one workgroup, ordered scan)
 //   decode_split   logits of the split's rows for a group of heads (each lane
 //                  owns one 16-byte piece of a row; the pieces of a row are
-//                  summed with cross-lane adds), per-head max and exp2 in LDS,
+//                  summed with DPP lane moves), per-head max and exp2 in LDS,
 //                  then the p-weighted sum of the V rows; writes (max, sum,
 //                  acc[d]) per head, max in the base-2 logit domain
 //   decode_merge   per (layer, head): log-sum-exp merge of its unit's splits
@@ -65,6 +65,28 @@ __device__ __forceinline__ void load_piece(const __bf16* p, float (&x)[8]) {
   }
 }
 
+// Sum of x over the LPR consecutive lanes that hold one row's pieces (LPR in
+// {8, 16, 32}), left in every one of them.  Within a 16-lane row the partners
+// come from DPP lane moves on the vector ALU (no LDS traffic): row mirror
+// (lane p and 15 - p), half-row mirror (p and p ^ 7) and two quad swaps (p ^ 2,
+// p ^ 1); the XOR masks 15, 7, 2 and 1 together reach all 16 lanes, so each
+// lane ends with the sum over the whole group (8 lanes: the last three).  A
+// 32-lane group first adds the other half through a lane shuffle.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (LPR == 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (LPR >= 16) x += dpp_mov<0x140>(x);  // row mirror
+  x += dpp_mov<0x141>(x);                            // row half mirror
+  x += dpp_mov<0x4E>(x);                             // quad permute [2, 3, 0, 1]
+  x += dpp_mov<0xB1>(x);                             // quad permute [1, 0, 3, 2]
+  return x;
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 
@@ -105,7 +127,8 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a) {
   constexpr int RPI = kThreads / LPR;      // rows per iteration of the workgroup
   constexpr int ITERS = kDecodeRows / RPI;
   static_assert(kDecodeRows % RPI == 0, "whole iterations");
-  static_assert(kDecodeRows == kThreads, "one row per thread in the softmax step");
+  constexpr int RPT = kDecodeRows / kThreads;   // rows per thread in the softmax step
+  static_assert(kDecodeRows % kThreads == 0, "whole rows per thread in the softmax step");
   __shared__ float zs[kDecodeRows][kHG];
   __shared__ float red[kWaves][kHG];
   __shared__ float racc[kWaves][kHG][D];
@@ -138,8 +161,12 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a) {
     float qf[kHG][EPL];
 #pragma unroll
     for (int j = 0; j < kHG; ++j) {
+      if (h0 + j < a.G) {
+        load_piece(qbase + (h0 + j) * D, qf[j]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) qf[j][e] = h0 + j < a.G ? to_f32(qbase[(h0 + j) * D + e]) : 0.f;
+        for (int e = 0; e < EPL; ++e) qf[j][e] = 0.f;
+      }
     }
     // logits of the split's rows
 #pragma unroll 4
@@ -157,22 +184,23 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a) {
         z[j] = acc;
       }
 #pragma unroll
-      for (int off = LPR / 2; off >= 1; off >>= 1) {
-#pragma unroll
-        for (int j = 0; j < kHG; ++j) z[j] += __shfl_xor(z[j], off, 64);
-      }
+      for (int j = 0; j < kHG; ++j) z[j] = row_sum<LPR>(z[j]);
       if (piece == 0) {
 #pragma unroll
         for (int j = 0; j < kHG; ++j) zs[rloc][j] = row < r1 ? z[j] * a.c1 : -INFINITY;
       }
     }
     __syncthreads();
-    // per-head max and sum over the split; thread t owns row t
-    float zt[kHG], mx[kHG], sm[kHG];
+    // per-head max and sum over the split; thread t owns rows t + q * kThreads
+    float zt[RPT][kHG], mx[kHG], sm[kHG];
 #pragma unroll
     for (int j = 0; j < kHG; ++j) {
-      zt[j] = zs[tid][j];
-      float m = zt[j];
+      float m = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        zt[q][j] = zs[tid + q * kThreads][j];
+        m = fmaxf(m, zt[q][j]);
+      }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
       if (lane == 0) red[wave][j] = m;
@@ -187,9 +215,14 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a) {
     __syncthreads();  // red is rewritten below
 #pragma unroll
     for (int j = 0; j < kHG; ++j) {
-      const float p = tid < r1 - r0 ? exp2_hw(zt[j] - mx[j]) : 0.f;
-      zs[tid][j] = p;
-      float t = p;
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < RPT; ++q) {
+        const int r = tid + q * kThreads;
+        const float p = r < r1 - r0 ? exp2_hw(zt[q][j] - mx[j]) : 0.f;
+        zs[r][j] = p;
+        t += p;
+      }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
       if (lane == 0) red[wave][j] = t;

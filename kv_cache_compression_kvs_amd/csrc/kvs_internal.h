@@ -125,7 +125,7 @@ inline SelectWs select_ws_layout(const kvs_problem& p) {
 // Decode over a ragged cache: rows per split workgroup, and the workspace
 // (split prefix, per-split partial max / sum / accumulators) for at most
 // max_rows kept rows in total.
-constexpr int kDecodeRows = 256;
+constexpr int kDecodeRows = 512;
 
 struct DecodeWs {
   int64_t slots = 0;  // split workgroups: ceil(max_rows / kDecodeRows) + units

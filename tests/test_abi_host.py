@@ -356,7 +356,7 @@ def test_decode_workspace_and_errors(K):
     p = prob(K)
     units, G = 4, 4
     b = K.kvs_decode_workspace_bytes(p, 1000)
-    slots = -(-1000 // 256) + units
+    slots = -(-1000 // 512) + units   # 512-row splits, one ragged tail per unit
     assert b >= slots * G * (2 + 128) * 4 + (units + 1) * 8
     assert K.kvs_decode_workspace_bytes(p, -1) == 0
 
