@@ -5,7 +5,9 @@
 // order (score descending, position ascending), listed ascending together
 // with the sinks [0, S).  Up to 32K candidates per (layer, KV head), one
 // 1024-thread workgroup owns one (layer, KV head) with its keys cached in
-// LDS; longer caches use the multi-workgroup select further below.
+// LDS; up to 128K candidates a 512-thread workgroup per (layer, KV head)
+// streams the keys twice (further below), and longer caches and the global
+// eviction use the multi-workgroup select at the end.
 //
 //  1. Scores become order-preserving 32-bit keys (sign-magnitude flip, -0 read
 //     as +0), cached in LDS (the query selection's chunks can exceed the cache;
@@ -22,6 +24,7 @@
 //     position its rank: S + above_before + min(equal_before, e).
 // Integer-only atomics on counts: the result does not depend on scheduling.
 #include <algorithm>
+#include <type_traits>
 
 #include "kvs_device.h"
 #include "kvs_internal.h"
@@ -93,7 +96,7 @@ __device__ __forceinline__ void wave_count(uint32_t* hist, bool active, uint32_t
   for (int r = 0; r < kPeel; ++r) {
     if (act == 0ull) return;  // the same on every lane
     const int leader = __ffsll((unsigned long long)act) - 1;
-    const uint32_t lb = __shfl(bin, leader, 64);
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
     const uint64_t same = act & __ballot(bin == lb);
     if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
     act &= ~same;
@@ -301,6 +304,523 @@ __global__ __launch_bounds__(kThreads) void query_select_kernel(QueryArgs a) {
   select_body<CACHED>(srow, keys, hw, wsum, pick, out, len, nq, c0);
 }
 
+
+// ---------------------------------------------------------------------------
+// Per-unit select for long caches: kSelSingleMax < candidates <= kLongMax.
+//
+// One 512-thread workgroup per (layer, KV head).  The cost of a pass over the
+// unit's keys is the work per key, which one CU does alone, so the common
+// path streams the keys once with a few operations per key:
+//   sample  8K keys (512 blocks of 16 consecutive positions, evenly spread,
+//           held in registers) are histogrammed on their top 12 bits and then,
+//           inside the two bins that matter, on the next 10.  That brackets
+//           the keys whose rank in the sample lies within 4 standard
+//           deviations (binomial) of the expected rank of tau, the need-th
+//           best: thresholds Thi (upper, inclusive) and Tlo (lower, inclusive).
+//   pass    every key above Thi is marked in a bitmap of the unit's candidates
+//           (one ballot per 64 consecutive keys) and counted; the keys in
+//           [Tlo, Thi] are counted and stored in LDS with their positions, one
+//           region per wave.
+// The counts are exact: if fewer than need keys lie above Thi and at least
+// need lie at or above Tlo, and every region held its keys, then tau is among
+// the stored keys.  Otherwise (heavy ties, or a sample far from the data) the
+// kernel starts over without the sample: histograms of the keys' top 12 bits,
+// then the next 10 and the last 10 (one read each, as far as needed) give the
+// bin of tau, and one more read marks the keys above it and stores or marks
+// the bin.  Either way an 8-bit radix select over the stored keys gives tau
+// and e (the number of keys equal to tau that are kept); stored keys above tau
+// join the bitmap and those equal to it a second one, and an ordered sweep
+// over the bitmaps (consecutive words per thread, a block scan of the counts)
+// writes every marked-above position and the e lowest tied ones, ascending.
+// The sample only steers the work; the result does not depend on it.
+constexpr int kLT = 512;
+constexpr int kLW = kLT / 64;
+constexpr int kLBatch = 16;                 // keys per thread per streaming step
+constexpr int64_t kLongMax = 128 * 1024;    // candidates per unit (bitmaps of 16 KiB each)
+constexpr int kLongWords = (int)(kLongMax / 32);
+constexpr int kCandMax = 5120;              // (key, position) pairs stored in LDS
+constexpr int kRegion = kCandMax / kLW;     // store region of one wave in the sampled pass
+constexpr int kSampleBlocks = 512;          // sampled blocks of 16 consecutive keys
+constexpr int kSampleKeys = kSampleBlocks * 16;
+constexpr int kSPT = kSampleKeys / kLT;     // sampled keys per thread
+constexpr double kSigmas = 4.0;
+static_assert(2 * kCandMax >= 4096 + 2 * 1024, "the sample histograms share the store");
+
+// Calls f(i, v, valid) for the scores v of the keys [0, nc) in steps of
+// kLT * kLBatch: key i = base + j * kLT + tid, so each wave covers 64
+// consecutive keys per j.  Full steps use buffer loads at scalar offsets (the
+// row is 4-byte aligned and every offset lies inside it); the ragged last
+// step uses loads clamped into the row.  Each step's loads are issued before
+// any of its keys is used.
+template <typename F>
+__device__ __forceinline__ void stream_scores(const float* srow, int64_t nc, F&& f) {
+  const int tid = threadIdx.x;
+  constexpr int kStep = kLT * kLBatch;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(srow), (short)0, (int)(nc * 4), kBufferFlags);
+  const int nfull = (int)(nc / kStep);
+  for (int st = 0; st < nfull; ++st) {
+    uint32_t v[kLBatch];
+#pragma unroll
+    for (int j = 0; j < kLBatch; ++j)
+      v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, (st * kStep + j * kLT) * 4, 0);
+#pragma unroll
+    for (int j = 0; j < kLBatch; ++j) f((int64_t)st * kStep + j * kLT + tid, __uint_as_float(v[j]), true);
+  }
+  const int64_t base = (int64_t)nfull * kStep;
+  if (base < nc) {
+    float v[kLBatch];
+#pragma unroll
+    for (int j = 0; j < kLBatch; ++j) v[j] = srow[min(base + (int64_t)j * kLT + tid, nc - 1)];
+#pragma unroll
+    for (int j = 0; j < kLBatch; ++j) {
+      const int64_t i = base + (int64_t)j * kLT + tid;
+      f(i, v[j], i < nc);
+    }
+  }
+}
+
+// The smallest non-NaN float whose key is >= u, so that for every non-NaN x,
+// order_key(x) >= u exactly when x >= it (NaN when no float qualifies: then
+// the comparison is false for every x).
+__device__ __forceinline__ float key_floor_float(uint64_t u) {
+  if (u <= 0x007FFFFFull) return -INFINITY;               // at or below the key of -inf
+  if (u > 0xFF800000ull) return __uint_as_float(0x7FC00000u);  // above the key of +inf
+  if (u >= 0x80000000ull) return __uint_as_float((uint32_t)u & 0x7FFFFFFFu);  // +0 .. +inf
+  if (u == 0x7FFFFFFFull) return 0.f;                     // no key: -0 reads as +0
+  return __uint_as_float(~(uint32_t)u);                  // negative floats
+}
+
+// Bin of the target-th largest key (1-based) of a histogram of nb bins, each
+// thread summing nb / kLT consecutive bins from the top; writes (bin, count
+// of the bins above it) to out[0..1].  Call with 1 <= target <= the total.
+__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t nb, uint32_t target,
+                                         uint32_t* wsum, uint32_t* out) {
+  const int tid = threadIdx.x;
+  const uint32_t per = nb / kLT;
+  uint32_t c = 0u;
+  for (uint32_t q = 0; q < per; ++q) c += hist[nb - 1u - tid * per - q];
+  uint32_t tot;
+  const uint32_t cum = block_scan<kLT>(c, wsum, &tot);
+  if (cum >= target && cum - c < target) {
+    uint32_t run = cum - c;
+    for (uint32_t q = 0; q < per; ++q) {
+      const uint32_t bin = nb - 1u - tid * per - q;
+      const uint32_t h = hist[bin];
+      if (run + h >= target) {
+        out[0] = bin;
+        out[1] = run;
+        break;
+      }
+      run += h;
+    }
+  }
+}
+
+// The 8-bit digit of a 256-bin histogram where the count from the top
+// reaches rem, found by one wave (lane l holds bins 255-4l .. 252-4l): writes
+// (digit, count of the bins above it) to out[0..1].  1 <= rem <= the total.
+__device__ __forceinline__ void pick_digit_wave(const uint32_t* h8, uint32_t rem, uint32_t* out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t b[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) b[q] = h8[255 - 4 * lane - q];
+  const uint32_t c = b[0] + b[1] + b[2] + b[3];
+  uint32_t cum = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(cum, off, 64);
+    if (lane >= off) cum += y;
+  }
+  if (cum >= rem && cum - c < rem) {
+    uint32_t run = cum - c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (run + b[q] >= rem) {
+        out[0] = 255u - (uint32_t)(4 * lane + q);
+        out[1] = run;
+        break;
+      }
+      run += b[q];
+    }
+  }
+}
+
+// The need-th best key (tau) and e among the keys stored in per-wave regions
+// (region w holds n[w] keys at keys + w * stride).  prefix / mask hold the
+// bits already fixed (every stored key matches them) and rem the rank to
+// find among the stored keys; 8-bit digits from bit s_top down.  On return
+// prefix is tau and rem is e.
+__device__ __forceinline__ void resolve_regions(const uint32_t* keys, int stride, const uint32_t* n,
+                                                int s_top, uint32_t& prefix, uint32_t& mask,
+                                                uint32_t& rem, uint32_t* h8, uint32_t* st) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t* mine = keys + wave * stride;
+  const uint32_t nw = n[wave];
+  for (int s = s_top;; s -= 8) {
+    const int sh = s > 0 ? s : 0;
+    if (tid < 256) h8[tid] = 0u;
+    __syncthreads();
+    for (uint32_t b0 = 0; b0 < nw; b0 += 64) {
+      const uint32_t i = b0 + lane;
+      const bool in = i < nw;
+      const uint32_t x = in ? mine[i] : 0u;
+      wave_count(h8, in && (x & mask) == prefix, (x >> sh) & 255u, lane);
+    }
+    __syncthreads();
+    if (wave == 0) pick_digit_wave(h8, rem, st);
+    __syncthreads();
+    prefix |= st[0] << sh;
+    mask |= 255u << sh;
+    rem -= st[1];
+    if (sh == 0) break;
+  }
+}
+
+// Two workgroups per CU (at most 128 VGPRs): more units than CUs still run in one round.
+__global__ __launch_bounds__(kLT, 4) void select_long_kernel(SelArgs a) {
+  __shared__ uint32_t store[2 * kCandMax];  // sample histograms, then keys | positions
+  __shared__ __attribute__((aligned(8))) uint32_t gtb[kLongWords];  // candidates above tau
+  __shared__ uint32_t eqb[kLongWords];      // candidates equal to tau
+  __shared__ uint32_t h8[256];
+  __shared__ uint32_t wsum[2 * kLW];
+  __shared__ uint32_t cnt_s[2 * kLW];       // per wave: keys above the bracket, keys stored
+  __shared__ uint32_t st[8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t unit = blockIdx.x;
+  const int64_t l = unit / a.Hkv, g = unit % a.Hkv;
+  const int64_t kl = a.t.k[l];
+  const int64_t N = a.N;
+  const int64_t S = a.S < N ? a.S : N;
+  const float* srow = a.scores + unit * N + S;
+  int32_t* out = a.kept + a.t.off[l] + g * kl;
+  const int64_t nc = N - S;  // in (kSelSingleMax, kLongMax]
+  const int64_t need = kl - S;
+
+  for (int64_t i = tid; i < S; i += kLT) out[i] = (int32_t)i;
+  if (need <= 0) return;  // only the sinks (uniform over the workgroup)
+  int32_t* dst = out + S;
+  if (need >= nc) {       // every candidate
+    for (int64_t i = tid; i < nc; i += kLT) dst[i] = (int32_t)(S + i);
+    return;
+  }
+  const int64_t words = (nc + 31) / 32;
+  uint32_t prefix = 0u, mask = 0u, rem = 0u;
+  bool sampled = true;
+
+  // ---- sample: the bracket [Tlo, Thi] --------------------------------------
+  // ranks (1-based, from the top) of the bracket's ends in the sample
+  const double pk = (double)need / (double)nc;
+  const double mu = pk * kSampleKeys;
+  const double sd = sqrt(kSampleKeys * pk * (1.0 - pk));
+  const int64_t r_hi = (int64_t)floor(mu - kSigmas * sd - 2.0);
+  const int64_t r_lo = (int64_t)ceil(mu + kSigmas * sd + 2.0);
+  const bool has_hi = r_hi >= 1;
+  const bool has_lo = r_lo <= kSampleKeys;
+  uint64_t Thi = 0xFFFFFFFFull, Tlo = 0ull;  // keys in [Tlo, Thi] are stored, above Thi marked
+  if (has_hi || has_lo) {
+    uint32_t sk[kSPT];
+#pragma unroll
+    for (int r = 0; r < kSPT; ++r) {
+      const int j = r * kLT + tid;  // block j / 16, key j % 16
+      const int64_t b0 = (int64_t)(j >> 4) * (nc - 16) / (kSampleBlocks - 1);
+      sk[r] = order_key(srow[b0 + (j & 15)]);
+    }
+    uint32_t* h1 = store;          // 4096 bins
+    uint32_t* h2a = store + 4096;  // 1024 bins inside the upper end's bin
+    uint32_t* h2b = store + 5120;  // 1024 bins inside the lower end's bin
+    for (int b = tid; b < 4096 + 2048; b += kLT) store[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSPT; ++r) wave_count(h1, true, sk[r] >> 20, lane);
+    __syncthreads();
+    if (has_hi) find_bin(h1, 4096u, (uint32_t)r_hi, wsum, st);
+    if (has_lo) find_bin(h1, 4096u, (uint32_t)r_lo, wsum, st + 2);
+    __syncthreads();
+    const uint32_t bin_hi = st[0], above_hi = st[1], bin_lo = st[2], above_lo = st[3];
+#pragma unroll
+    for (int r = 0; r < kSPT; ++r) {
+      const uint32_t b = sk[r] >> 20, sub = (sk[r] >> 10) & 1023u;
+      wave_count(h2a, has_hi && b == bin_hi, sub, lane);
+      wave_count(h2b, has_lo && b == bin_lo, sub, lane);
+    }
+    __syncthreads();
+    if (has_hi) find_bin(h2a, 1024u, (uint32_t)r_hi - above_hi, wsum, st + 4);
+    if (has_lo) find_bin(h2b, 1024u, (uint32_t)r_lo - above_lo, wsum, st + 6);
+    __syncthreads();
+    if (has_hi) Thi = (bin_hi << 20) | (st[4] << 10) | 1023u;
+    if (has_lo) Tlo = (bin_lo << 20) | (st[6] << 10);
+  }
+  for (int64_t w = tid; w < words; w += kLT) {
+    gtb[w] = 0u;
+    eqb[w] = 0u;
+  }
+  __syncthreads();  // st and store are rewritten below
+
+  // ---- one pass: mark above Thi, store [Tlo, Thi] ----------------------------
+  // For a non-NaN score x: key above Thi <=> x >= f_above, key >= Tlo <=> x >= f_lo.
+  // Stored keys hold the raw score bits until the pass ends.
+  {
+    const float f_above = key_floor_float(Thi + 1);
+    const float f_lo = key_floor_float(Tlo);
+    uint32_t n_ab = 0u, n_in = 0u;  // this wave's counts (uniform)
+    uint32_t* kreg = store + wave * kRegion;
+    uint32_t* preg = store + kCandMax + wave * kRegion;
+    // Steps of kPB keys per thread, double-buffered: the next step's loads are
+    // in flight while this step's keys are compared.
+    constexpr int kPB = kLBatch / 2;
+    constexpr int kStep = kLT * kPB;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(srow), (short)0, (int)(nc * 4), kBufferFlags);
+    const int nsteps = (int)((nc + kStep - 1) / kStep);
+    auto load_step = [&](float (&v)[kPB], int sp) __attribute__((always_inline)) {
+      const int64_t base = (int64_t)sp * kStep;
+      if (base + kStep <= nc) {
+#pragma unroll
+        for (int j = 0; j < kPB; ++j)
+          v[j] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+              rs, tid * 4, (int)(base + j * kLT) * 4, 0));
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPB; ++j) v[j] = srow[min(base + (int64_t)j * kLT + tid, nc - 1)];
+      }
+    };
+    // FULL: every key of the step lies inside the row (a compile-time fact,
+    // so full steps carry no per-key bounds test).
+    auto use_step = [&](auto full_tag, const float (&v)[kPB], int sp) __attribute__((always_inline)) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      const int64_t base = (int64_t)sp * kStep;
+      // lane q of words_v holds bitmap word q of this step's 2 * kPB words of this
+      // wave: keys base + (q / 2) * kLT + wave * 64 + 32 * (q % 2) .. + 31
+      uint32_t words_v = 0u;
+#pragma unroll
+      for (int j = 0; j < kPB; ++j) {
+        const int64_t i = base + (int64_t)j * kLT + tid;
+        uint64_t ab = __ballot(v[j] >= f_above);
+        uint64_t ge = __ballot(v[j] >= f_lo);
+        if (!FULL) {
+          const uint64_t vm = __ballot(i < nc);
+          ab &= vm;
+          ge &= vm;
+        }
+        if (__ballot(v[j] != v[j]) != 0ull) {  // NaN scores: compare their keys instead
+          const uint32_t x = order_key(v[j]);
+          const bool valid = FULL || i < nc;
+          ab = __ballot(valid && (uint64_t)x > Thi);
+          ge = __ballot(valid && (uint64_t)x >= Tlo);
+        }
+        const uint64_t ib = ge & ~ab;
+        n_ab += (uint32_t)__popcll(ab);
+        const uint32_t half = (lane & 1) ? (uint32_t)(ab >> 32) : (uint32_t)ab;
+        if ((lane >> 1) == j) words_v = half;
+        if (ib != 0ull) {
+          if ((ib >> lane) & 1ull) {
+            const uint32_t s = n_in + __builtin_amdgcn_mbcnt_hi((uint32_t)(ib >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)ib, 0u));
+            if (s < (uint32_t)kRegion) {
+              kreg[s] = __float_as_uint(v[j]);
+              preg[s] = (uint32_t)i;
+            }
+          }
+          n_in += (uint32_t)__popcll(ib);
+        }
+      }
+      if (lane < 2 * kPB) {
+        const int64_t w = base / 32 + (lane >> 1) * (kLT / 32) + wave * 2 + (lane & 1);
+        if (w < words) gtb[w] = words_v;
+      }
+    };
+    auto use_any = [&](const float (&v)[kPB], int sp) __attribute__((always_inline)) {
+      if ((int64_t)(sp + 1) * kStep <= nc) use_step(std::true_type{}, v, sp);
+      else use_step(std::false_type{}, v, sp);
+    };
+    float va[kPB], vb[kPB];
+    load_step(va, 0);
+    for (int sp = 0; sp < nsteps; sp += 2) {
+      if (sp + 1 < nsteps) load_step(vb, sp + 1);
+      use_any(va, sp);
+      if (sp + 2 < nsteps) load_step(va, sp + 2);
+      if (sp + 1 < nsteps) use_any(vb, sp + 1);
+    }
+    // raw score bits to keys
+    for (uint32_t i = lane; i < min(n_in, (uint32_t)kRegion); i += 64) kreg[i] = order_key(__uint_as_float(kreg[i]));
+    if (lane == 0) {
+      cnt_s[wave] = n_ab;
+      cnt_s[kLW + wave] = n_in;
+    }
+  }
+  __syncthreads();
+  {
+    uint32_t above = 0u, inside = 0u;
+#pragma unroll
+    for (int w = 0; w < kLW; ++w) {
+      above += cnt_s[w];
+      inside += cnt_s[kLW + w];
+      sampled = sampled && cnt_s[kLW + w] <= (uint32_t)kRegion;
+    }
+    sampled = sampled && above < (uint32_t)need && (uint64_t)above + inside >= (uint64_t)need;
+    rem = (uint32_t)need - above;
+  }
+
+  if (sampled) {
+    // bits shared by every key of [Tlo, Thi], in whole 8-bit digits
+    const uint32_t common = (uint32_t)Tlo ^ (uint32_t)Thi;
+    const int lead = common ? __builtin_clz(common) : 32;
+    const int fixed = (lead / 8) * 8;
+    mask = fixed ? (fixed == 32 ? 0xFFFFFFFFu : ~(0xFFFFFFFFu >> fixed)) : 0u;
+    prefix = (uint32_t)Thi & mask;
+    if (fixed < 32)
+      resolve_regions(store, kRegion, cnt_s + kLW, 24 - fixed, prefix, mask, rem, h8, st);
+    const uint32_t nw = cnt_s[kLW + wave];
+    for (uint32_t i = lane; i < nw; i += 64) {
+      const uint32_t x = store[wave * kRegion + i];
+      const uint32_t pos = store[kCandMax + wave * kRegion + i];
+      if (x > prefix) atomicOr(&gtb[pos >> 5], 1u << (pos & 31u));
+      else if (x == prefix) atomicOr(&eqb[pos >> 5], 1u << (pos & 31u));
+    }
+    __syncthreads();
+  } else {
+    // ---- without the sample: histograms of [31:20], then [19:10], then [9:0]
+    for (int64_t w = tid; w < words; w += kLT) gtb[w] = 0u;
+    rem = (uint32_t)need;
+    prefix = 0u;
+    mask = 0u;
+    uint32_t cnt = 0u;
+    int shift = 20, bits = 12;
+    for (;;) {
+      const uint32_t nb = 1u << bits;
+      for (uint32_t b = tid; b < nb; b += kLT) store[b] = 0u;
+      __syncthreads();
+      stream_scores(srow, nc, [&](int64_t, float v, bool valid) __attribute__((always_inline)) {
+        const uint32_t x = order_key(v);
+        wave_count(store, valid && (x & mask) == prefix, (x >> shift) & (nb - 1u), lane);
+      });
+      __syncthreads();
+      find_bin(store, nb, rem, wsum, st);
+      __syncthreads();
+      const uint32_t bin = st[0];
+      prefix |= bin << shift;
+      mask |= (nb - 1u) << shift;
+      rem -= st[1];
+      cnt = store[bin];
+      __syncthreads();  // st and store are rewritten below
+      if (cnt <= (uint32_t)kCandMax || shift == 0) break;
+      shift -= 10;
+      bits = 10;
+    }
+    const bool resolved = shift == 0;  // prefix is tau itself
+    if (tid == 0) st[3] = 0u;
+    __syncthreads();
+    stream_scores(srow, nc, [&](int64_t i, float v, bool valid) __attribute__((always_inline)) {
+      const uint32_t x = order_key(v);
+      const uint32_t hi = x & mask;
+      const uint64_t above = __ballot(valid && hi > prefix);
+      const bool in = valid && hi == prefix;
+      const uint64_t inb = __ballot(in);
+      const int64_t i0 = i - lane;
+      if (lane < 2 && i0 + 32 * lane < nc) {
+        const int64_t w = i0 / 32 + lane;
+        gtb[w] = (uint32_t)(above >> (32 * lane));
+        if (resolved) eqb[w] = (uint32_t)(inb >> (32 * lane));
+      }
+      if (!resolved && inb != 0ull) {
+        uint32_t slot0 = 0u;
+        if (lane == 0) slot0 = atomicAdd(&st[3], (uint32_t)__popcll(inb));
+        slot0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)slot0);
+        if (in) {
+          const uint32_t s = slot0 + (uint32_t)__popcll(inb & ((1ull << lane) - 1ull));
+          if (s < (uint32_t)kCandMax) {
+            store[s] = x;
+            store[kCandMax + s] = (uint32_t)i;
+          }
+        }
+      }
+    });
+    __syncthreads();
+    if (!resolved) {
+      // the n stored keys as one region per wave of n / kLW (the last takes the rest)
+      const uint32_t n = min(st[3], (uint32_t)kCandMax);  // equals cnt
+      const uint32_t per = n / kLW;
+      __syncthreads();  // st is rewritten by the radix select
+      if (tid < kLW) cnt_s[kLW + tid] = tid == kLW - 1 ? n - per * (kLW - 1) : per;
+      __syncthreads();
+      resolve_regions(store, (int)per, cnt_s + kLW, shift - 8, prefix, mask, rem, h8, st);
+      for (uint32_t i = tid; i < n; i += kLT) {
+        const uint32_t x = store[i];
+        const uint32_t pos = store[kCandMax + i];
+        if (x > prefix) atomicOr(&gtb[pos >> 5], 1u << (pos & 31u));
+        else if (x == prefix) atomicOr(&eqb[pos >> 5], 1u << (pos & 31u));
+      }
+      __syncthreads();
+    }
+  }
+  const uint32_t e = rem;
+
+  // ---- ordered sweep over the bitmaps ----------------------------------------
+  // Wave w owns a contiguous range of words, taken 64 at a time, one per lane.
+  {
+    const int64_t wpw = ((words + kLW - 1) / kLW + 63) / 64 * 64;
+    const int64_t wb = min((int64_t)wave * wpw, words), we = min(wb + wpw, words);
+    uint32_t cg = 0u, ce = 0u;
+    for (int64_t w = wb + lane; w < we; w += 64) {
+      cg += (uint32_t)__popc(gtb[w]);
+      ce += (uint32_t)__popc(eqb[w]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      cg += __shfl_xor(cg, off, 64);
+      ce += __shfl_xor(ce, off, 64);
+    }
+    __syncthreads();  // cnt_s is rewritten
+    if (lane == 0) {
+      cnt_s[wave] = cg;
+      cnt_s[kLW + wave] = ce;
+    }
+    __syncthreads();
+    uint32_t gbase = 0u, ebase = 0u;
+    for (int w = 0; w < wave; ++w) {
+      gbase += cnt_s[w];
+      ebase += cnt_s[kLW + w];
+    }
+    for (int64_t c0 = wb; c0 < we; c0 += 64) {
+      const int64_t w = c0 + lane;
+      const uint32_t G = w < we ? gtb[w] : 0u, E = w < we ? eqb[w] : 0u;
+      const uint32_t packed = ((uint32_t)__popc(G) << 16) | (uint32_t)__popc(E);  // <= 2048 each per chunk
+      uint32_t incl = packed;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      const uint32_t excl = incl - packed;
+      uint32_t gt_before = gbase + (excl >> 16);
+      uint32_t eq_before = ebase + (excl & 0xFFFFu);
+      uint32_t m = G | E;
+      while (m) {
+        const int b = __builtin_ctz(m);
+        m &= m - 1u;
+        const int64_t pos = w * 32 + b;
+        // ranks are < need by construction; the bound check only keeps a
+        // counting error from ever writing outside this list
+        if ((G >> b) & 1u) {
+          const uint64_t rank = (uint64_t)gt_before + min(eq_before, e);
+          if (rank < (uint64_t)need) dst[rank] = (int32_t)(S + pos);
+          ++gt_before;
+        } else {
+          if (eq_before < e) {
+            const uint64_t rank = (uint64_t)gt_before + eq_before;
+            if (rank < (uint64_t)need) dst[rank] = (int32_t)(S + pos);
+          }
+          ++eq_before;
+        }
+      }
+      gbase += tot >> 16;
+      ebase += tot & 0xFFFFu;
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Multi-workgroup radix select.
@@ -704,7 +1224,7 @@ int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t
   if (units <= 0 || p.n_cache <= 0) return 0;
   const int64_t nc = p.n_cache - std::min(p.n_sinks, p.n_cache);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (select_uses_multi(p)) return run_multi(p, scores, &t, 0, kept, nullptr, ws, st);
+  if (nc > kLongMax) return run_multi(p, scores, &t, 0, kept, nullptr, ws, st);
   SelArgs a;
   a.scores = scores;
   a.kept = kept;
@@ -712,9 +1232,11 @@ int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t
   a.S = p.n_sinks;
   a.Hkv = p.kv_heads;
   a.t = t;
-  (void)nc;  // <= kLdsKeys here: the candidates fit the LDS key cache
   TraceScope ts("select", st);
-  hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)units), dim3(kThreads), 0, st, a);
+  if (nc > kLdsKeys)
+    hipLaunchKernelGGL(select_long_kernel, dim3((unsigned)units), dim3(kLT), 0, st, a);
+  else
+    hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)units), dim3(kThreads), 0, st, a);
   return (int)hipGetLastError();
 }
 

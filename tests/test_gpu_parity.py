@@ -131,7 +131,14 @@ SEL = [
     (1, 1, 32773, 4, "uniform", [1000]),         # one candidate too many: global path
     (2, 1, 100003, 4, "sparse", [5000]),         # global path, ragged batches
     (1, 1, 131072, 4, "uniform", [2621]),
-    (1, 1, 131072, 4, "equal", [2621]),
+    (1, 1, 131072, 4, "equal", [2621]),          # every key equal: tau fixed by the histograms
+    (1, 1, 131076, 4, "uniform", [2621]),        # 128K candidates: the bitmaps exactly full
+    (1, 1, 131077, 4, "uniform", [3000]),        # one more: multi-workgroup select
+    (2, 1, 60000, 4, "narrow", [7000]),          # one top bin: refined over all three levels
+    (1, 1, 131072, 4, "coarse", [65000]),        # ~7.7K per level: refined, ties at tau
+    (1, 1, 50000, 4, "coarse", [20000]),         # ~2.9K per level: stored, ties at tau
+    (1, 1, 70000, 4, "tiny", [5000]),            # denormals and zeros
+    (1, 1, 40000, 4, "sparse", [39000]),         # tau among the zeros
     (2, 1, 700, 4, "uniform", [700]),            # keep everything
     (1, 1, 1, 0, "uniform", [1]),
     (1, 1, 3, 5, "uniform", [3]),                # N < S: all sinks

@@ -374,7 +374,9 @@ def score_tensor(units: int, n: int, n_sinks: int, kind: str = "uniform", seed: 
     """fp32 scores [units, n] in [0, 1] with a chosen tie structure.
 
     kind: "uniform" (continuous, ties improbable), "coarse" (values on a grid of
-    17 levels, so ties are everywhere), "equal" (all identical), "sparse"
+    17 levels, so ties are everywhere), "equal" (all identical), "narrow"
+    (every value within a relative 2^-12 of 0.3: a few thousand distinct
+    values, each repeated, all sharing their top 20 bits), "sparse"
     (mostly exact zeros with a few positives), "tiny" (values down to 1e-38,
     including denormals and zero).
     """
@@ -385,6 +387,8 @@ def score_tensor(units: int, n: int, n_sinks: int, kind: str = "uniform", seed: 
         s = torch.randint(0, 17, (units, n), generator=g).float() / 16.0
     elif kind == "equal":
         s = torch.full((units, n), 0.375)
+    elif kind == "narrow":
+        s = 0.3 * (1.0 + torch.rand(units, n, generator=g) * 2.0 ** -12)
     elif kind == "sparse":
         s = torch.rand(units, n, generator=g)
         s = torch.where(torch.rand(units, n, generator=g) < 0.97, torch.zeros_like(s), s)
