@@ -417,6 +417,64 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t nb, uint
   }
 }
 
+// find_bin for two targets with one block scan (t1 or t2 zero: not wanted);
+// writes (bin, count above) of t1 to out[0..1] and of t2 to out[2..3].
+__device__ __forceinline__ void find_bin2(const uint32_t* hist, uint32_t nb, uint32_t t1, uint32_t t2,
+                                          uint32_t* wsum, uint32_t* out) {
+  const int tid = threadIdx.x;
+  const uint32_t per = nb / kLT;
+  uint32_t c = 0u;
+  for (uint32_t q = 0; q < per; ++q) c += hist[nb - 1u - tid * per - q];
+  uint32_t tot;
+  const uint32_t cum = block_scan<kLT>(c, wsum, &tot);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t target = k ? t2 : t1;
+    if (target != 0u && cum >= target && cum - c < target) {
+      uint32_t run = cum - c;
+      for (uint32_t q = 0; q < per; ++q) {
+        const uint32_t bin = nb - 1u - tid * per - q;
+        const uint32_t h = hist[bin];
+        if (run + h >= target) {
+          out[2 * k] = bin;
+          out[2 * k + 1] = run;
+          break;
+        }
+        run += h;
+      }
+    }
+  }
+}
+
+// find_bin by one wave (lane l sums the nb / 64 bins nb-1-l*per .. from the
+// top), with no workgroup barrier; the writing lane stores (bin, count above).
+__device__ __forceinline__ void find_bin_wave(const uint32_t* hist, uint32_t nb, uint32_t target,
+                                              uint32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t per = nb / 64;
+  const uint32_t top = nb - 1u - (uint32_t)lane * per;  // this lane's highest bin
+  uint32_t c = 0u;
+  for (uint32_t q = 0; q < per; ++q) c += hist[top - q];
+  uint32_t cum = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(cum, off, 64);
+    if (lane >= off) cum += y;
+  }
+  if (cum >= target && cum - c < target) {
+    uint32_t run = cum - c;
+    for (uint32_t q = 0; q < per; ++q) {
+      const uint32_t h = hist[top - q];
+      if (run + h >= target) {
+        out[0] = top - q;
+        out[1] = run;
+        break;
+      }
+      run += h;
+    }
+  }
+}
+
 // The 8-bit digit of a 256-bin histogram where the count from the top
 // reaches rem, found by one wave (lane l holds bins 255-4l .. 252-4l): writes
 // (digit, count of the bins above it) to out[0..1].  1 <= rem <= the total.
@@ -535,8 +593,7 @@ __global__ __launch_bounds__(kLT, 4) void select_long_kernel(SelArgs a) {
 #pragma unroll
     for (int r = 0; r < kSPT; ++r) wave_count(h1, true, sk[r] >> 20, lane);
     __syncthreads();
-    if (has_hi) find_bin(h1, 4096u, (uint32_t)r_hi, wsum, st);
-    if (has_lo) find_bin(h1, 4096u, (uint32_t)r_lo, wsum, st + 2);
+    find_bin2(h1, 4096u, has_hi ? (uint32_t)r_hi : 0u, has_lo ? (uint32_t)r_lo : 0u, wsum, st);
     __syncthreads();
     const uint32_t bin_hi = st[0], above_hi = st[1], bin_lo = st[2], above_lo = st[3];
 #pragma unroll
@@ -546,12 +603,13 @@ __global__ __launch_bounds__(kLT, 4) void select_long_kernel(SelArgs a) {
       wave_count(h2b, has_lo && b == bin_lo, sub, lane);
     }
     __syncthreads();
-    if (has_hi) find_bin(h2a, 1024u, (uint32_t)r_hi - above_hi, wsum, st + 4);
-    if (has_lo) find_bin(h2b, 1024u, (uint32_t)r_lo - above_lo, wsum, st + 6);
+    if (has_hi && wave == 0) find_bin_wave(h2a, 1024u, (uint32_t)r_hi - above_hi, st + 4);
+    if (has_lo && wave == 1) find_bin_wave(h2b, 1024u, (uint32_t)r_lo - above_lo, st + 6);
     __syncthreads();
     if (has_hi) Thi = (bin_hi << 20) | (st[4] << 10) | 1023u;
     if (has_lo) Tlo = (bin_lo << 20) | (st[6] << 10);
   }
+  if (tid == 0) st[7] = 0u;  // set if the pass reads a NaN (read after the pass's barrier)
   for (int64_t w = tid; w < words; w += kLT) {
     gtb[w] = 0u;
     eqb[w] = 0u;
@@ -560,11 +618,13 @@ __global__ __launch_bounds__(kLT, 4) void select_long_kernel(SelArgs a) {
 
   // ---- one pass: mark above Thi, store [Tlo, Thi] ----------------------------
   // For a non-NaN score x: key above Thi <=> x >= f_above, key >= Tlo <=> x >= f_lo.
+  // A NaN fails both tests, so a unit with a NaN score is redone from its keys.
   // Stored keys hold the raw score bits until the pass ends.
   {
     const float f_above = key_floor_float(Thi + 1);
     const float f_lo = key_floor_float(Tlo);
     uint32_t n_ab = 0u, n_in = 0u;  // this wave's counts (uniform)
+    uint64_t nan_w = 0ull;          // lanes that read a NaN score
     uint32_t* kreg = store + wave * kRegion;
     uint32_t* preg = store + kCandMax + wave * kRegion;
     // Steps of kPB keys per thread, double-buffered: the next step's loads are
@@ -597,25 +657,17 @@ __global__ __launch_bounds__(kLT, 4) void select_long_kernel(SelArgs a) {
 #pragma unroll
       for (int j = 0; j < kPB; ++j) {
         const int64_t i = base + (int64_t)j * kLT + tid;
-        uint64_t ab = __ballot(v[j] >= f_above);
-        uint64_t ge = __ballot(v[j] >= f_lo);
-        if (!FULL) {
-          const uint64_t vm = __ballot(i < nc);
-          ab &= vm;
-          ge &= vm;
-        }
-        if (__ballot(v[j] != v[j]) != 0ull) {  // NaN scores: compare their keys instead
-          const uint32_t x = order_key(v[j]);
-          const bool valid = FULL || i < nc;
-          ab = __ballot(valid && (uint64_t)x > Thi);
-          ge = __ballot(valid && (uint64_t)x >= Tlo);
-        }
-        const uint64_t ib = ge & ~ab;
+        const bool valid = FULL || i < nc;
+        const bool up = valid && v[j] >= f_above;
+        const bool in = valid && v[j] >= f_lo && !(v[j] >= f_above);
+        nan_w |= __ballot(v[j] != v[j]);  // a NaN compares false: the unit starts over below
+        const uint64_t ab = __ballot(up);
+        const uint64_t ib = __ballot(in);
         n_ab += (uint32_t)__popcll(ab);
         const uint32_t half = (lane & 1) ? (uint32_t)(ab >> 32) : (uint32_t)ab;
         if ((lane >> 1) == j) words_v = half;
         if (ib != 0ull) {
-          if ((ib >> lane) & 1ull) {
+          if (in) {
             const uint32_t s = n_in + __builtin_amdgcn_mbcnt_hi((uint32_t)(ib >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)ib, 0u));
             if (s < (uint32_t)kRegion) {
@@ -648,6 +700,7 @@ __global__ __launch_bounds__(kLT, 4) void select_long_kernel(SelArgs a) {
     if (lane == 0) {
       cnt_s[wave] = n_ab;
       cnt_s[kLW + wave] = n_in;
+      if (nan_w) st[7] = 1u;
     }
   }
   __syncthreads();
@@ -659,6 +712,7 @@ __global__ __launch_bounds__(kLT, 4) void select_long_kernel(SelArgs a) {
       inside += cnt_s[kLW + w];
       sampled = sampled && cnt_s[kLW + w] <= (uint32_t)kRegion;
     }
+    sampled = sampled && st[7] == 0u;  // no NaN score (NaN keys order above +inf)
     sampled = sampled && above < (uint32_t)need && (uint64_t)above + inside >= (uint64_t)need;
     rem = (uint32_t)need - above;
   }
@@ -798,6 +852,16 @@ __global__ __launch_bounds__(kLT, 4) void select_long_kernel(SelArgs a) {
       uint32_t gt_before = gbase + (excl >> 16);
       uint32_t eq_before = ebase + (excl & 0xFFFFu);
       uint32_t m = G | E;
+      if (G == 0xFFFFFFFFu && E == 0u) {  // 32 consecutive kept positions, consecutive ranks
+        const uint64_t r0 = (uint64_t)gt_before + min(eq_before, e);
+        if (r0 + 32 <= (uint64_t)need) {
+          int32_t* o = dst + r0;
+          const int32_t p0 = (int32_t)(S + w * 32);
+#pragma unroll
+          for (int k = 0; k < 32; ++k) o[k] = p0 + k;
+        }
+        m = 0u;
+      }
       while (m) {
         const int b = __builtin_ctz(m);
         m &= m - 1u;

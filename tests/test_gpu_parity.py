@@ -160,6 +160,25 @@ def test_select_matches_oracle_exactly(K, case):
     assert np.array_equal(got[:total], want)
 
 
+@pytest.mark.parametrize("N", [6144, 40000, 140000])
+def test_select_nan_orders_above_inf(K, N):
+    """The ABI orders NaN above +inf; every select path (LDS-resident, one
+    workgroup streaming, multi-workgroup) agrees.  The oracle sees the NaNs as
+    2.0, above every other score here, which gives the same order."""
+    S, ks = 4, [1500]
+    scores = gen.score_tensor(2, N, S, "uniform", seed=N + 11)
+    g = torch.Generator().manual_seed(N)
+    nan_pos = torch.randint(S, N, (2, 40), generator=g)
+    scores.scatter_(1, nan_pos, float("nan"))
+    p = K.make_problem(1, 2, 2, 128, N, S, N - S, 1, torch.bfloat16)
+    kept = torch.full((2 * ks[0],), -7, dtype=torch.int32, device="cuda")
+    K.kvs_select(p, scores.cuda(), ks, kept)
+    torch.cuda.synchronize()
+    s64 = torch.nan_to_num(scores, nan=2.0).double().numpy().reshape(1, 2, N)
+    want = O.pack_kept(O.select(s64, ks, S))
+    assert np.array_equal(kept.cpu().numpy(), want)
+
+
 # --- compaction and append -----------------------------------------------------
 
 @pytest.mark.parametrize("dt,d,stride", [(torch.bfloat16, 128, 0), (torch.bfloat16, 64, 0),
