@@ -177,8 +177,7 @@ def test_block_loop_full(K):
     loop.reset()
     n = w.budget_m + w.block_len
     for b in range(w.n_blocks):
-        prev_k = loop.k[loop.cur][:, :, :loop.n].clone()
-        prev_v = loop.v[loop.cur][:, :, :loop.n].clone()
+        prev_k, prev_v = (t.clone() for t in loop.cache_view())
         if loop.step(b, x["k_tokens"], x["v_tokens"], x["q_steps"][b]):
             sc = loop.scores[:s.layers * s.kv_heads * n].view(s.layers, s.kv_heads, n).clone()
             kk = loop.kept.view(s.layers, s.kv_heads, w.budget_m).clone()

@@ -315,11 +315,12 @@ def test_block_loop_teacher_forced(K):
     for b, rec in enumerate(recs):
         nb = min(w.block_len, kt.shape[2] - b * w.block_len)
         n_prev = rec["n_cache"] - nb
-        loop.cur = 0
-        loop.n = n_prev
-        if n_prev:
-            loop.k[0][:, :, :n_prev] = torch.from_numpy(rec["k"][:, :, :n_prev]).bfloat16().cuda()
-            loop.v[0][:, :, :n_prev] = torch.from_numpy(rec["v"][:, :, :n_prev]).bfloat16().cuda()
+        # before the first compression the oracle's cache is the token prefix,
+        # which the driver holds in place: leave it so (that compression reads
+        # the token buffer itself); afterwards start each step from the oracle
+        if scored:
+            loop.load_cache(torch.from_numpy(rec["k"]).bfloat16().cuda(),
+                            torch.from_numpy(rec["v"]).bfloat16().cuda(), n_prev)
         before_k = torch.from_numpy(rec["k"]).bfloat16().cuda()
         did = loop.step(b, kt, vt, qs[b])
         torch.cuda.synchronize()
