@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
   }
   auto compute_tile = [&](const uint8_t* buf) __attribute__((always_inline)) {
     constexpr int NS = 2 * KS;      // MFMAs (and update slices) per block
-    constexpr int EPS = 16 / NS;    // elements per slice of each query block
+    static_assert(NS >= 4, "at least two slices take the previous block's terms");
     bf16x8 af[2][KS];               // fragments of the current and the next key block
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) af[0][ks] = afrag(buf, 0, ks);
@@ -203,10 +203,15 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
           // next block's fragment ks now, so that block starts without an LDS wait
           if (kb + 1 < NB) af[cur ^ 1][i >> 1] = afrag(buf, kb + 1, i >> 1);
         }
+        // The previous block's 32 terms go to slices 2 .. NS-1 (p0's first):
+        // its last MFMAs (slices NS-2, NS-1) may still be writing them during
+        // slices 0 and 1, and a read there would wait for them.
 #pragma unroll
-        for (int u = 0; u < EPS; ++u) {
-          t0 += exp2_hw(fmaf(p0[i * EPS + u], c1, -m0));
-          t1 += exp2_hw(fmaf(p1[i * EPS + u], c1, -m1));
+        for (int e = 0; e < 32; ++e) {
+          if (2 + (e * (NS - 2)) / 32 == i) {
+            if (e < 16) t0 += exp2_hw(fmaf(p0[e], c1, -m0));
+            else t1 += exp2_hw(fmaf(p1[e - 16], c1, -m1));
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
