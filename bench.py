@@ -313,6 +313,8 @@ def main():
     # ---- float64 oracle on a bounded sample of the same workload ---------------
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, kl)
+        if "next_rows" in rec:
+            oracle_rows(w, x, scores, rec["next_rows"], gen)
     print(json.dumps(rec), flush=True)
 
 
@@ -440,6 +442,86 @@ def profiled_traffic(workload, kernel):
             h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
             return int(m.group(2)) if h == m.group(4) else None
     return None
+
+
+def oracle_rows(w, x, scores, rows, gen):
+    """The oracle beside each next row, on a bounded sample of the row's own
+    input, in the row's unit: algorithmic GB/s of the sample (ms per call for
+    the clustering, which is timed whole)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import oracle as O
+
+    s = w.shape
+    L, Hq, Hkv, d, N, S = s.layers, s.q_heads, s.kv_heads, s.head_dim, s.n_cache, s.n_sinks
+    G, eb, U = s.group, s.elem_bytes(), s.layers * s.kv_heads
+    threads = int(max((p.get("num_threads", 1) for p in threadpool_info()), default=1))
+
+    def f64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    def base(value, unit, sample):
+        return {"value": round(value, 3), "unit": unit, "cores": threads, "kind": "oracle",
+                "sample": sample}
+
+    def timed(fn):
+        """Seconds per call of fn, repeated until half a second has passed (at most
+        50 calls), and the last call's result."""
+        n, t0 = 0, time.perf_counter()
+        while True:
+            out = fn()
+            n += 1
+            dt = time.perf_counter() - t0
+            if dt >= 0.5 or n >= 50:
+                return dt / n, out
+
+    sc = scores.view(L, Hkv, N).cpu().numpy()
+    if "f1_query_select" in rows:
+        r = rows["f1_query_select"]
+        dt, _ = timed(lambda: O.select_queries(O.token_sums_f32(sc), N, S, s.chunk_size, r["rho"]))
+        r["cpu_baseline"] = base(r["algorithmic_bytes"] / dt / 1e9, "GB/s",
+                                 f"the whole row: token sums of {U} units x {N} and the selection "
+                                 f"of every chunk, {dt:.3f} s per call")
+    if "f2_global" in rows:
+        r = rows["f2_global"]
+        us = 8  # the first 8 units (layer 0), the budget scaled to them
+        need = (r["total_budget"] - U * S) * us // U
+        tot = need + us * S
+        s8 = sc[:1, :us].astype(np.float64)
+        t_sel, kept = timed(lambda: O.select_global(s8, tot, S))
+        k0, v0 = f64(x["k"][:1, :us]), f64(x["v"][:1, :us])
+        t_cmp, (ko, vo) = timed(lambda: O.compact_ragged(k0, v0, kept))
+        _, off = O.pack_ragged(kept)
+        q1 = np.random.default_rng(0).standard_normal((1, us * G, d))
+        t_dec, _ = timed(lambda: O.decode_attention(q1, ko, vo, off, us))
+        sel_b, cmp_b = 4 * us * N + 4 * tot, tot * (2 * d * eb * 2 + 4)
+        dec_b = tot * 2 * d * eb + us * G * d * (eb + 4)
+        what = f"{us} of {U} units (layer 0), budget {tot} scaled to them"
+        r["select_compact"]["cpu_baseline"] = base((sel_b + cmp_b) / (t_sel + t_cmp) / 1e9, "GB/s",
+                                                   f"{what}, {t_sel + t_cmp:.3f} s per call")
+        r["decode_ragged"]["cpu_baseline"] = base(dec_b / t_dec / 1e9, "GB/s",
+                                                  f"{what}: {us * G} query heads, "
+                                                  f"{t_dec:.4f} s per call")
+    if "f3_similarity" in rows:
+        r = rows["f3_similarity"]
+        kf, kb = f64(x["k"][:1, :2]), f64(x["v"][:1, :2])
+        dt, _ = timed(lambda: O.key_similarity(kf, kb))
+        r["cpu_baseline"] = base(2 * 2 * N * d * eb / dt / 1e9, "GB/s",
+                                 f"layer 0, 2 of {Hkv} KV heads x {N} positions, "
+                                 f"{dt:.3f} s per call")
+    if "f4_episodes" in rows:
+        r = rows["f4_episodes"]
+        emb = gen.episode_embeddings(r["segments"], r["dim"], r["episodes"], seed=0)
+        xe = emb["x"].double().numpy()
+        init, qe = xe[emb["init_index"].numpy()], emb["q"].double().numpy()
+
+        def row():
+            cent, assign = O.kmeans(xe, init, r["lloyd_rounds"])
+            O.medoids(xe, assign, r["episodes"])
+            return O.nearest_centroid(qe, cent)
+        dt, _ = timed(row)
+        r["cpu_baseline"] = base(dt * 1e3, "ms per call", f"the whole row, {dt:.2f} s per call")
 
 
 def cpu_baseline(w, x, budget_s, kl):
