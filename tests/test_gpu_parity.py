@@ -179,6 +179,58 @@ def test_select_nan_orders_above_inf(K, N):
     assert np.array_equal(kept.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("T", [1100, 900])
+def test_block_loop_ragged_and_uncompressed_streams(K, T):
+    """Token streams cut short of the workload's: at T = 1100 the first
+    compression reads the token buffer's first 1040 rows in place and the next
+    one a ragged 60-row block behind the kept cache; at T = 900 nothing is ever
+    compressed, and the cache, held as the token buffer's rows until asked
+    for, must then be copied out exactly."""
+    from kv_cache_compression_kvs_amd import drivers
+    w = SMALL["epicache_block_loop"]
+    s = w.shape
+    x = gen.block_loop_inputs(w)
+    kt, vt = x["k_tokens"][:, :, :T].contiguous(), x["v_tokens"][:, :, :T].contiguous()
+    nblk = -(-T // w.block_len)
+    qs = x["q_steps"][:nblk]
+    recs = O.block_loop(f64(kt), f64(vt), f64(qs), w.block_len, w.budget_m, s.n_sinks)
+    loop = drivers.BlockLoop(s.layers, s.q_heads, s.kv_heads, s.head_dim, torch.bfloat16,
+                             w.block_len, w.budget_m, s.n_sinks, s.q_per_chunk)
+    pos = {"p": torch.zeros(s.layers, s.kv_heads, 0, dtype=torch.long)}
+
+    def on_step(b, lp, did):
+        nb = min(w.block_len, T - b * w.block_len)
+        newp = torch.arange(b * w.block_len, b * w.block_len + nb).expand(s.layers, s.kv_heads, nb)
+        p = torch.cat([pos["p"], newp], dim=2)
+        if did:
+            kk = lp.kept.view(s.layers, s.kv_heads, w.budget_m).long().cpu()
+            p = torch.gather(p, 2, kk)
+        pos["p"] = p
+
+    ktc, vtc = kt.cuda(), vt.cuda()
+    scored = loop.run(ktc, vtc, qs.cuda(), on_step=on_step)
+    torch.cuda.synchronize()
+    assert scored == sum("kept" in r for r in recs)
+    final = recs[-1]["pos"]
+    if "kept" in recs[-1]:
+        final = np.take_along_axis(final, np.stack(recs[-1]["kept"]), axis=2)
+    got = pos["p"].numpy()
+    assert got.shape == final.shape
+    mismatch = sum(len(set(got[l, g]) ^ set(final[l, g]))
+                   for l in range(s.layers) for g in range(s.kv_heads))
+    assert mismatch <= 0.01 * got.size
+    if not scored:
+        vk, vv = loop.cache_view()   # still the token rows, nothing copied
+        assert vk.data_ptr() == ktc.data_ptr() and vk.shape[2] == T
+    ck, cv = loop.cache()
+    assert ck.shape[2] == got.shape[2]
+    for l in range(s.layers):
+        for g in range(s.kv_heads):
+            idx = torch.from_numpy(got[l, g]).cuda()
+            assert torch.equal(ck[l, g], ktc[l, g, idx])
+            assert torch.equal(cv[l, g], vtc[l, g, idx])
+
+
 # --- compaction and append -----------------------------------------------------
 
 @pytest.mark.parametrize("dt,d,stride", [(torch.bfloat16, 128, 0), (torch.bfloat16, 64, 0),
