@@ -150,7 +150,7 @@ int kvs_score(const kvs_problem* p, const void* q, const void* k, float* scores,
  * Scores compare as floats (-0 equals +0); NaN orders above +inf.
  * ws: device workspace of kvs_workspace_bytes(p) bytes, 256-byte aligned; it
  * is used (and then required, else KVS_E_NULL / KVS_E_WORKSPACE /
- * KVS_E_ALIGN) only when N - S exceeds 32768 candidates per (l, g).
+ * KVS_E_ALIGN) only when N - S exceeds 131072 candidates per (l, g).
  */
 int kvs_select(const kvs_problem* p, const float* scores, const int64_t* k_per_layer,
                int32_t* kept, void* ws, size_t ws_bytes, void* stream);

@@ -89,9 +89,14 @@ int launch_append(int32_t slabs, int64_t row_bytes, const void* src, int64_t src
 // workspace it carves (per-unit mode for long caches, and the global mode).
 constexpr int64_t kSelSpan = 4096;
 constexpr int64_t kSelSingleMax = 32 * 1024;
+// Per-unit selection streams up to this many candidates per unit in one
+// workgroup (bitmaps of them in LDS) and needs no workspace up to it.
+constexpr int64_t kSelLongMax = 128 * 1024;
 
+// Per-unit selection takes the multi-workgroup path (and the caller's
+// workspace) beyond kSelLongMax candidates per unit.
 inline bool select_uses_multi(const kvs_problem& p) {
-  return p.n_cache - (p.n_sinks < p.n_cache ? p.n_sinks : p.n_cache) > kSelSingleMax;
+  return p.n_cache - (p.n_sinks < p.n_cache ? p.n_sinks : p.n_cache) > kSelLongMax;
 }
 
 struct SelectWs {

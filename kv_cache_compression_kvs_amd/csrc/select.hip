@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void query_select_kernel(QueryArgs a) {
 constexpr int kLT = 512;
 constexpr int kLW = kLT / 64;
 constexpr int kLBatch = 16;                 // keys per thread per streaming step
-constexpr int64_t kLongMax = 128 * 1024;    // candidates per unit (bitmaps of 16 KiB each)
+constexpr int64_t kLongMax = kSelLongMax;   // candidates per unit (bitmaps of 16 KiB each)
 constexpr int kLongWords = (int)(kLongMax / 32);
 constexpr int kCandMax = 5120;              // (key, position) pairs stored in LDS
 constexpr int kRegion = kCandMax / kLW;     // store region of one wave in the sampled pass
@@ -1288,7 +1288,7 @@ int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t
   if (units <= 0 || p.n_cache <= 0) return 0;
   const int64_t nc = p.n_cache - std::min(p.n_sinks, p.n_cache);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (nc > kLongMax) return run_multi(p, scores, &t, 0, kept, nullptr, ws, st);
+  if (select_uses_multi(p)) return run_multi(p, scores, &t, 0, kept, nullptr, ws, st);
   SelArgs a;
   a.scores = scores;
   a.kept = kept;

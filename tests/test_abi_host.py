@@ -295,7 +295,7 @@ def test_workspace_covers_the_multi_workgroup_select(K):
 
 def test_select_requires_workspace_only_for_long_caches(K):
     h = raw(K)
-    p = prob(K, n_cache=40000, chunk_size=40000)     # 39,996 candidates > 32K
+    p = prob(K, n_cache=140000, chunk_size=140000)   # 139,996 candidates > 128K
     ks = (ctypes.c_int64 * 2)(100, 200)
     ws = K.kvs_workspace_bytes(p)
     assert h.kvs_select(ctypes.byref(p), FAKE, ks, FAKE, None, 0, None) == 1
