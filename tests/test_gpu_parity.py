@@ -74,6 +74,8 @@ EDGE = [
     (1, 12, 3, 128, 2049, 4, 2045, 300, "bf16"), # G = 4, rows spill into a second row block
     (1, 4, 2, 128, 4, 4, 16, 5, "bf16"),         # every position a sink
     (1, 4, 2, 128, 6, 10, 16, 5, "bf16"),        # N < S
+    (1, 8, 2, 64, 6000, 4, 5996, 64, "bf16"),    # d = 64, one chunk, keys split over workgroups
+    (2, 8, 2, 128, 9001, 4, 8997, 40, "bf16"),   # d = 128, one chunk, split keys, odd N
     (1, 2, 1, 64, 999, 1, 400, 9, "f32"),        # fp32, d = 64, ragged
     (2, 4, 2, 128, 700, 4, 333, 20, "f32"),      # fp32, d = 128
 ]
