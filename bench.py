@@ -404,11 +404,19 @@ def episode_row(K, torch, gen, E, dev):
     tr = K.kvs_trace_summary()
     a = assign.cpu()
     sizes = torch.bincount(a.long(), minlength=E)
-    same_pairs = int((sizes.double() ** 2).sum())
-    # algorithmic: the same-cluster pairs, a subtract and a fused multiply-add
-    # per element; executed: the tiled kernel forms every pair
+    same_pairs = int((sizes.double() * (sizes.double() - 1) / 2).sum())
+    # algorithmic: each distinct same-cluster pair once (a distance serves both
+    # points), a subtract and a fused multiply-add per element; executed: the
+    # 32 x 32 tile pairs (I <= J) of the cluster-sorted order whose cluster
+    # ranges overlap, each formed whole
+    tile = 32
+    key = torch.sort(a.long()).values
+    tiles = (n + tile - 1) // tile
+    first = key[torch.arange(tiles) * tile]
+    last = key[torch.clamp(torch.arange(tiles) * tile + tile - 1, max=n - 1)]
+    formed = sum(int((last[i] >= first[i:]).sum()) for i in range(tiles))
     medoid_flops = 3 * dim * same_pairs
-    executed_flops = 3 * dim * n * n
+    executed_flops = 3 * dim * formed * tile * tile
     med_ms = tr["medoid_tile"]["avg_ms"] if "medoid_tile" in tr else None
     return {"segments": n, "dim": dim, "episodes": E, "lloyd_rounds": rounds,
             "ms_total": round(sum(v["total_ms"] for v in tr.values()) / reps, 5),

@@ -361,9 +361,12 @@ int kvs_sensitivity(int32_t layers, const double* similarity, double* sens);
  *   points of its cluster (device fp32 [n] out); medoid[e] = the member of
  *   cluster e with the least total, ties to the lower index, -1 if empty
  *   (device int32 [clusters] out).  assign: device int32 [n] in [0, clusters).
- *   n <= 64 * 65535.  ws: device workspace of kvs_medoids_workspace_bytes(n,
- *   dim, clusters) bytes (about n * n / 16 bytes: one partial sum per point
- *   and 64-point tile), 256-byte aligned.
+ *   A label outside [0, clusters) is not an error: such a point sums its
+ *   distances to the points with the same label and belongs to no medoid.
+ *   n <= 32 * 65535.  ws: device workspace of kvs_medoids_workspace_bytes(n,
+ *   dim, clusters) bytes (about n * n / 8 + 8 n bytes: one partial sum per
+ *   point and 32-point tile, and the points' order by cluster), 256-byte
+ *   aligned.
  * kvs_match_episodes: episode[j] = the centroid nearest to query row j (as in
  *   the assignment), q: device [m, dim], episode: device int32 [m].
  * Errors: KVS_E_SHAPE (sizes above), KVS_E_NULL, KVS_E_ALIGN (rows 16-byte,

@@ -16,10 +16,14 @@
 //   centroid_final   per (cluster, dimension): the blocks' partials in a fixed
 //                    order in float64, divided by the member count; an empty
 //                    cluster keeps its centroid.
-//   medoid_tile      pairwise distances in 64 x 64 tiles (4 x 4 pairs per
-//                    thread, 32-dimension chunks staged in LDS), summed per row
-//                    over the pairs that share a cluster; medoid_sum adds the
-//                    tiles' row sums in a fixed order.
+//   medoid_order     one workgroup: a stable counting sort of the points by
+//                    cluster, so that each cluster is one run of positions.
+//   medoid_tile      pairwise distances in 64 x 64 tiles of sorted positions,
+//                    only for the tile pairs I <= J whose cluster ranges
+//                    overlap; each distance of a same-cluster pair is formed
+//                    once and added to both of its points' sums.
+//   medoid_sum       a point's total over the tiles that hold its cluster, in
+//                    tile order.
 //   medoid_pick      per cluster, the member with the least total, ties to
 //                    the lower index (-1 if the cluster is empty).
 #include <cmath>
@@ -34,6 +38,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBlockPoints = 32;   // points per centroid_partial workgroup
+constexpr int kBatch = 32;         // points whose loads centroid_partial issues together
 constexpr int kSliceDims = 1024;   // dimensions per centroid_partial workgroup
 
 __global__ __launch_bounds__(kThreads) void nearest_kernel(const float* __restrict__ x, int64_t n,
@@ -42,14 +47,25 @@ __global__ __launch_bounds__(kThreads) void nearest_kernel(const float* __restri
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (i >= n) return;  // a whole wave
+  // the lane's pieces of the row (dimensions 4 lane + 256 p .. +3), loaded once
+  constexpr int kPieces = (int)(kMaxEmbedDim / 256);
   const float* xr = x + i * D;
+  float4 xa[kPieces];
+#pragma unroll
+  for (int p = 0; p < kPieces; ++p) {
+    const int64_t k = 4 * lane + 256 * p;
+    if (k < D) xa[p] = *reinterpret_cast<const float4*>(xr + k);
+  }
   float best = INFINITY;
   int32_t arg = 0;
   for (int32_t e = 0; e < E; ++e) {
     const float* cr = c + (int64_t)e * D;
     float acc = 0.f;
-    for (int64_t k = 4 * lane; k < D; k += 256) {
-      const float4 a = *reinterpret_cast<const float4*>(xr + k);
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) {
+      const int64_t k = 4 * lane + 256 * p;
+      if (k >= D) break;
+      const float4 a = xa[p];
       const float4 b = *reinterpret_cast<const float4*>(cr + k);
       const float d0 = a.x - b.x, d1 = a.y - b.y, d2 = a.z - b.z, d3 = a.w - b.w;
       acc = fmaf(d0, d0, acc);
@@ -86,18 +102,30 @@ __global__ __launch_bounds__(kThreads) void centroid_partial(const float* __rest
   int32_t cnt[kMaxClusters];
 #pragma unroll
   for (int e = 0; e < kMaxClusters; ++e) cnt[e] = 0;
+  // points in index order, their loads issued kBatch at a time so that the
+  // batch's latencies overlap
   const int64_t p0 = blk * kBlockPoints, p1 = min(p0 + kBlockPoints, n);
-  for (int64_t i = p0; i < p1; ++i) {
-    const int32_t a = assign[i];
-    if (mine) {
-      const float4 v = *reinterpret_cast<const float4*>(x + i * D + d0);
-      acc[a][4 * tid + 0] += v.x;
-      acc[a][4 * tid + 1] += v.y;
-      acc[a][4 * tid + 2] += v.z;
-      acc[a][4 * tid + 3] += v.w;
+  for (int64_t i0 = p0; i0 < p1; i0 += kBatch) {
+    int32_t a[kBatch];
+    float4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t i = i0 + u;
+      a[u] = i < p1 ? assign[i] : -1;
+      if (mine && i < p1) v[u] = *reinterpret_cast<const float4*>(x + i * D + d0);
     }
 #pragma unroll
-    for (int e = 0; e < kMaxClusters; ++e) cnt[e] += a == e;
+    for (int u = 0; u < kBatch; ++u) {
+      if (a[u] < 0) continue;
+      if (mine) {
+        acc[a[u]][4 * tid + 0] += v[u].x;
+        acc[a[u]][4 * tid + 1] += v[u].y;
+        acc[a[u]][4 * tid + 2] += v[u].z;
+        acc[a[u]][4 * tid + 3] += v[u].w;
+      }
+#pragma unroll
+      for (int e = 0; e < kMaxClusters; ++e) cnt[e] += a[u] == e;
+    }
   }
   if (mine) {
     for (int e = 0; e < E; ++e) {
@@ -122,6 +150,7 @@ __global__ __launch_bounds__(kThreads) void centroid_final(const float* __restri
   if (k >= D) return;
   double s = 0.0;
   int64_t cnt = 0;
+#pragma unroll 8
   for (int64_t b = 0; b < blocks; ++b) {
     s += (double)psum[(b * E + e) * D + k];
     cnt += pcnt[b * E + e];
@@ -135,99 +164,245 @@ __global__ __launch_bounds__(kThreads) void copy_f32(const float* __restrict__ s
   if (i < n) dst[i] = src[i];
 }
 
-// Pairwise distances in 64 x 64 tiles: thread (ty, tx) of the 16 x 16 grid owns
-// the 4 x 4 pairs (i0 + 4 ty + r, j0 + 4 tx + c); the two row sets stream through
-// LDS in chunks of 32 dimensions (stored transposed, so the inner loop reads
-// four consecutive rows of one dimension as one 16-byte word).  Each pair adds
-// its Euclidean distance to row i's sum if i and j share a cluster; a row's sum
-// over the tile goes to part[j tile][i].
-constexpr int kTile = 64;
-constexpr int kChunk = 32;
+// Medoid totals: total_i = sum over the members j of i's cluster of |x_i - x_j|.
+// Positions are grouped into tiles of kTile; a tile pair (I, J), I <= J, is
+// formed when the two tiles hold a common group.
+constexpr int kTile = 32;
+constexpr int kOrderThreads = 1024;
+constexpr int kGroups = kMaxClusters + 1;
 
-__global__ __launch_bounds__(kThreads) void medoid_tile(const float* __restrict__ x, int64_t n,
-                                                        int64_t D,
-                                                        const int32_t* __restrict__ assign,
-                                                        float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) float xi[kChunk][kTile];
-  __shared__ __attribute__((aligned(16))) float xj[kChunk][kTile];
-  __shared__ float rsum[16][kTile];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int64_t i0 = (int64_t)blockIdx.x * kTile, j0 = (int64_t)blockIdx.y * kTile;
-  float acc[4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-  }
-  // loader: thread t copies rows (t / 8) and (t / 8) + 32, dimensions
-  // 4 * (t % 8) .. +3 of the chunk, for both row sets
-  const int lr = tid >> 3, ld = (tid & 7) * 4;
-  for (int64_t k0 = 0; k0 < D; k0 += kChunk) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = lr + 32 * h;
-      const int64_t gi = min(i0 + row, n - 1), gj = min(j0 + row, n - 1);
-      const bool in_d = k0 + ld < D;  // D is a multiple of 4
-      float4 a = in_d ? *reinterpret_cast<const float4*>(x + gi * D + k0 + ld) : float4{0, 0, 0, 0};
-      float4 b = in_d ? *reinterpret_cast<const float4*>(x + gj * D + k0 + ld) : float4{0, 0, 0, 0};
-      xi[ld + 0][row] = a.x;
-      xi[ld + 1][row] = a.y;
-      xi[ld + 2][row] = a.z;
-      xi[ld + 3][row] = a.w;
-      xj[ld + 0][row] = b.x;
-      xj[ld + 1][row] = b.y;
-      xj[ld + 2][row] = b.z;
-      xj[ld + 3][row] = b.w;
+// medoid_order sorts the points by cluster, stably (one workgroup, chunks of
+// 1024 points in index order; a point's place is its cluster's running start
+// plus the count of same-cluster points before it in the chunk, from per-wave
+// ballots).  Outputs: perm[p], the point at sorted position p; skey[p], its
+// group; cstart[g], the first position of group g.  Groups are the clusters
+// and, last, every label outside [0, clusters), so perm is always a full
+// permutation; the distance sums still compare the labels themselves.
+// It also lists the tile pairs to form: tile I pairs with the tiles J from I
+// up to the one holding the last position of I's last group, and pstart[I] is
+// the number of pairs of the tiles before I (pstart[tiles] = all of them).
+__global__ __launch_bounds__(kOrderThreads) void medoid_order(const int32_t* __restrict__ assign,
+                                                              int64_t n, int32_t E,
+                                                              int32_t* __restrict__ perm,
+                                                              int32_t* __restrict__ skey,
+                                                              int32_t* __restrict__ cstart,
+                                                              uint32_t* __restrict__ pstart) {
+  constexpr int W = kOrderThreads / 64;
+  __shared__ uint32_t wc[W][kGroups];      // per wave and group: count in the current chunk
+  __shared__ uint32_t base[kGroups];       // per group: next free position
+  __shared__ uint32_t gstart[kGroups + 1]; // per group: first position; [E + 1] = n
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t below = (1ull << lane) - 1ull;  // lanes under this one
+  auto group = [&](int64_t i) __attribute__((always_inline)) -> int {
+    if (i >= n) return -1;
+    const int32_t a = assign[i];
+    return (a >= 0 && a < E) ? a : E;
+  };
+  uint32_t total = 0;  // thread g <= E: size of group g
+  for (int64_t c0 = 0; c0 < n; c0 += kOrderThreads) {
+    const int g = group(c0 + tid);
+    for (int k = 0; k <= E; ++k) {
+      const uint64_t m = __ballot(g == k);
+      if (lane == 0) wc[wave][k] = (uint32_t)__popcll(m);
     }
     __syncthreads();
-#pragma unroll 8
-    for (int k = 0; k < kChunk; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(&xi[k][ty * 4]);
-      const float4 b = *reinterpret_cast<const float4*>(&xj[k][tx * 4]);
-      const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float d = av[r] - bv[c];
-          acc[r][c] = fmaf(d, d, acc[r][c]);
-        }
-      }
-    }
+    if (tid <= E)
+      for (int w = 0; w < W; ++w) total += wc[w][tid];
     __syncthreads();
   }
-  int32_t ai[4], aj[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t i = i0 + ty * 4 + r, j = j0 + tx * 4 + r;
-    ai[r] = i < n ? assign[i] : -1;
-    aj[r] = j < n ? assign[j] : -2;
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float t = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (ai[r] == aj[c]) t += sqrtf(acc[r][c]);
-    rsum[tx][ty * 4 + r] = t;
+  if (tid <= E) wc[0][tid] = total;  // the group sizes, for thread 0's scan
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t s = 0;
+    for (int k = 0; k <= E; ++k) {
+      base[k] = s;
+      gstart[k] = s;
+      cstart[k] = (int32_t)s;
+      s += wc[0][k];
+    }
+    gstart[E + 1] = s;  // n
+    cstart[E + 1] = (int32_t)s;
   }
   __syncthreads();
-  if (tid < kTile) {
-    float t = 0.f;
+  if (wave == 0) {  // the tile-pair list, one tile per lane, 64 tiles per step
+    const int64_t tiles = ceil_div(n, kTile);
+    uint32_t carry = 0;
+    for (int64_t t0 = 0; t0 < tiles; t0 += 64) {
+      const int64_t I = t0 + lane;
+      uint32_t cnt = 0;
+      if (I < tiles) {
+        const uint32_t last = (uint32_t)min(I * kTile + kTile - 1, n - 1);
+        int g = 0;
+        while (gstart[g + 1] <= last) ++g;  // the group holding position `last`
+        cnt = (uint32_t)((gstart[g + 1] - 1) / kTile - I + 1);
+      }
+      uint32_t inc = cnt;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) t += rsum[q][tid];
-    if (i0 + tid < n) part[(int64_t)blockIdx.y * n + i0 + tid] = t;
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += y;
+      }
+      if (I < tiles) pstart[I] = carry + inc - cnt;
+      carry += __shfl(inc, 63, 64);
+    }
+    if (lane == 0) pstart[tiles] = carry;
+  }
+  for (int64_t c0 = 0; c0 < n; c0 += kOrderThreads) {
+    const int64_t i = c0 + tid;
+    const int g = group(i);
+    uint64_t mine = 0;
+    for (int k = 0; k <= E; ++k) {
+      const uint64_t m = __ballot(g == k);
+      if (g == k) mine = m;
+      if (lane == 0) wc[wave][k] = (uint32_t)__popcll(m);
+    }
+    __syncthreads();
+    if (g >= 0) {
+      uint32_t pos = base[g] + (uint32_t)__popcll(mine & below);
+      for (int w = 0; w < wave; ++w) pos += wc[w][g];
+      perm[pos] = (int32_t)i;
+      skey[pos] = g;
+    }
+    __syncthreads();
+    if (tid <= E)
+      for (int w = 0; w < W; ++w) base[tid] += wc[w][tid];
+    __syncthreads();
   }
 }
 
-// total[i] = sum over the j tiles of part[jt][i], in tile order.
+// One workgroup per listed tile pair (I, J), I <= J (workgroups past the list
+// exit at once; the listed ones come first, so they spread over the chip).
+// Thread (ty, tx) of the 16 x 16 grid owns the 2 x 2 pairs of rows ty, ty + 16
+// of tile I and columns tx, tx + 16 of tile J.  The two tiles' rows stream
+// through LDS in chunks of 64 dimensions (rows padded by 16 bytes, so the 16
+// consecutive rows a quarter-wave reads fall in distinct banks); each step
+// reads four dimensions of each of a thread's four rows as 16-byte words.
+// Each chunk's global loads are issued into registers before the previous
+// chunk is computed, so their latency hides behind it.  A same-cluster pair's
+// distance goes to its row sum (rows of I, to part[J][p]) and, for I < J, to
+// its column sum (rows of J, to part[I][p]): each distance is formed once and
+// serves both points.
+constexpr int kChunk = 64;
+constexpr int kPad = kChunk + 4;
+constexpr int kTileThreads = (kTile / 2) * (kTile / 2);
+constexpr int kLoads = 2 * kTile * kChunk / 4 / kTileThreads;  // 16-byte loads per thread per chunk
+static_assert(kLoads * kTileThreads * 4 == 2 * kTile * kChunk, "loader covers both tiles");
+
+__global__ __launch_bounds__(kTileThreads) void medoid_tile(const float* __restrict__ x, int64_t n,
+                                                            int64_t D,
+                                                            const int32_t* __restrict__ assign,
+                                                            const int32_t* __restrict__ perm,
+                                                            const uint32_t* __restrict__ pstart,
+                                                            int64_t tiles,
+                                                            float* __restrict__ part) {
+  constexpr int TS = kTile / 2;  // threads per tile side
+  const uint32_t b = blockIdx.x;
+  if (b >= pstart[tiles]) return;  // uniform
+  int64_t lo = 0, hi = tiles - 1;  // the last tile I with pstart[I] <= b
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (pstart[mid] <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  const int64_t I = lo, J = I + (b - pstart[I]);
+  const int64_t i0 = I * kTile, j0 = J * kTile;
+  __shared__ __attribute__((aligned(16))) float xs[2][kTile][kPad];  // [tile I / J][row][dim]
+  __shared__ float rbuf[TS][kTile];  // [tx][row of I]: row sums over the thread's columns
+  __shared__ float cbuf[TS][kTile];  // [ty][row of J]: column sums over the thread's rows
+  const int tid = threadIdx.x, tx = tid % TS, ty = tid / TS;
+  // loader: load h of thread t copies dimensions 4 (L % CQ) .. +3 of the
+  // chunk for row (L / CQ) % kTile of tile L / (CQ kTile), L = t + h kTileThreads
+  constexpr int CQ = kChunk / 4;  // 16-byte pieces per row and chunk
+  const float* lsrc[kLoads];
+  float* ldst[kLoads];
+  int ld[kLoads];
+#pragma unroll
+  for (int h = 0; h < kLoads; ++h) {
+    const int L = tid + h * kTileThreads;
+    const int set = L / (CQ * kTile), row = (L / CQ) % kTile;
+    ld[h] = (L % CQ) * 4;
+    const int64_t pos = min((set ? j0 : i0) + row, n - 1);
+    lsrc[h] = x + (int64_t)perm[pos] * D + ld[h];
+    ldst[h] = &xs[set][row][ld[h]];
+  }
+  float4 pf[kLoads];
+  auto fetch = [&](int64_t k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < kLoads; ++h)
+      pf[h] = k0 + ld[h] < D ? *reinterpret_cast<const float4*>(lsrc[h] + k0)  // D % 4 == 0
+                             : float4{0.f, 0.f, 0.f, 0.f};
+  };
+  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  fetch(0);
+  for (int64_t k0 = 0; k0 < D; k0 += kChunk) {
+#pragma unroll
+    for (int h = 0; h < kLoads; ++h) *reinterpret_cast<float4*>(ldst[h]) = pf[h];
+    __syncthreads();
+    if (k0 + kChunk < D) fetch(k0 + kChunk);
+#pragma unroll 4
+    for (int k = 0; k < kChunk; k += 4) {
+      const float4 a0 = *reinterpret_cast<const float4*>(&xs[0][ty][k]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&xs[0][ty + TS][k]);
+      const float4 b0 = *reinterpret_cast<const float4*>(&xs[1][tx][k]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&xs[1][tx + TS][k]);
+      const float av[2][4] = {{a0.x, a0.y, a0.z, a0.w}, {a1.x, a1.y, a1.z, a1.w}};
+      const float bv[2][4] = {{b0.x, b0.y, b0.z, b0.w}, {b1.x, b1.y, b1.z, b1.w}};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const float d = av[r][q] - bv[c][q];
+            acc[r][c] = fmaf(d, d, acc[r][c]);
+          }
+    }
+    __syncthreads();
+  }
+  int32_t ai[2], aj[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int64_t pi = i0 + ty + r * TS, pj = j0 + tx + r * TS;
+    ai[r] = pi < n ? assign[perm[pi]] : -1;
+    aj[r] = pj < n ? assign[perm[pj]] : -2;
+  }
+  float dist[2][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) dist[r][c] = ai[r] == aj[c] ? sqrtf(acc[r][c]) : 0.f;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) rbuf[tx][ty + r * TS] = dist[r][0] + dist[r][1];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) cbuf[ty][tx + c * TS] = dist[0][c] + dist[1][c];
+  __syncthreads();
+  if (tid < kTile) {
+    float t = 0.f;
+    for (int q = 0; q < TS; ++q) t += rbuf[q][tid];
+    if (i0 + tid < n) part[J * n + i0 + tid] = t;
+  } else if (tid < 2 * kTile && I < J) {
+    const int col = tid - kTile;
+    float t = 0.f;
+    for (int q = 0; q < TS; ++q) t += cbuf[q][col];
+    if (j0 + col < n) part[I * n + j0 + col] = t;
+  }
+}
+
+// total[perm[p]] = sum of part[jt][p] over the tiles jt that hold p's group,
+// in tile order.  Every such tile pair overlaps p's own tile, so medoid_tile
+// wrote each of these entries.
 __global__ __launch_bounds__(kThreads) void medoid_sum(const float* __restrict__ part, int64_t n,
-                                                       int64_t jtiles, float* __restrict__ total) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= n) return;
+                                                       const int32_t* __restrict__ perm,
+                                                       const int32_t* __restrict__ skey,
+                                                       const int32_t* __restrict__ cstart,
+                                                       float* __restrict__ total) {
+  const int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (p >= n) return;
+  const int g = skey[p];
+  const int64_t t0 = cstart[g] / kTile, t1 = (cstart[g + 1] - 1) / kTile;
   float t = 0.f;
-  for (int64_t jt = 0; jt < jtiles; ++jt) t += part[jt * n + i];
-  total[i] = t;
+  for (int64_t jt = t0; jt <= t1; ++jt) t += part[jt * n + p];
+  total[perm[p]] = t;
 }
 
 __global__ __launch_bounds__(kThreads) void medoid_pick(const int32_t* __restrict__ assign,
@@ -313,20 +488,51 @@ int launch_kmeans(const float* x, int64_t n, int64_t dim, int32_t clusters, cons
   return launch_nearest(x, n, dim, centroids, clusters, assign, stream);
 }
 
+// Medoid workspace: part [tiles][n] f32 (tiles of kTile positions), then
+// perm [n], skey [n], cstart [kGroups + 1] int32 and pstart [tiles + 1]
+// uint32, each piece 256-byte aligned.
+namespace {
+struct MedoidWs {
+  size_t off_perm, off_skey, off_cstart, off_pstart, bytes;
+};
+MedoidWs medoid_ws_layout(int64_t n) {
+  auto r256 = [](size_t b) { return (b + 255) & ~size_t(255); };
+  MedoidWs w;
+  w.off_perm = r256(sizeof(float) * (size_t)(ceil_div(n, kTile) * n));
+  w.off_skey = w.off_perm + r256(sizeof(int32_t) * (size_t)n);
+  w.off_cstart = w.off_skey + r256(sizeof(int32_t) * (size_t)n);
+  w.off_pstart = w.off_cstart + r256(sizeof(int32_t) * (kGroups + 1));
+  w.bytes = w.off_pstart + r256(sizeof(uint32_t) * (size_t)(ceil_div(n, kTile) + 1));
+  return w;
+}
+}  // namespace
+
 int launch_medoids(const float* x, int64_t n, int64_t dim, const int32_t* assign, int32_t clusters,
                    int32_t* medoid, float* totals, void* ws, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (n > 0) {
     const int64_t tiles = ceil_div(n, kTile);
-    float* part = static_cast<float*>(ws);
+    const MedoidWs w = medoid_ws_layout(n);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    float* part = reinterpret_cast<float*>(base);
+    int32_t* perm = reinterpret_cast<int32_t*>(base + w.off_perm);
+    int32_t* skey = reinterpret_cast<int32_t*>(base + w.off_skey);
+    int32_t* cstart = reinterpret_cast<int32_t*>(base + w.off_cstart);
+    uint32_t* pstart = reinterpret_cast<uint32_t*>(base + w.off_pstart);
     {
+      TraceScope ts("medoid_order", st);
+      hipLaunchKernelGGL(medoid_order, dim3(1), dim3(kOrderThreads), 0, st, assign, n, clusters,
+                         perm, skey, cstart, pstart);
+    }
+    {
+      // every tile pair I <= J at most; the list's length is known on the device only
       TraceScope ts("medoid_tile", st);
-      hipLaunchKernelGGL(medoid_tile, dim3((unsigned)tiles, (unsigned)tiles), dim3(kThreads), 0, st,
-                         x, n, dim, assign, part);
+      hipLaunchKernelGGL(medoid_tile, dim3((unsigned)(tiles * (tiles + 1) / 2)), dim3(kTileThreads),
+                         0, st, x, n, dim, assign, perm, pstart, tiles, part);
     }
     TraceScope ts("medoid_sum", st);
     hipLaunchKernelGGL(medoid_sum, dim3((unsigned)ceil_div(n, kThreads)), dim3(kThreads), 0, st,
-                       part, n, tiles, totals);
+                       part, n, perm, skey, cstart, totals);
   }
   TraceScope ts("medoid_pick", st);
   hipLaunchKernelGGL(medoid_pick, dim3(1), dim3(kThreads), 0, st, assign, totals, n, clusters,
@@ -334,8 +540,6 @@ int launch_medoids(const float* x, int64_t n, int64_t dim, const int32_t* assign
   return (int)hipGetLastError();
 }
 
-size_t medoid_ws_bytes(int64_t n) {
-  return ((size_t)sizeof(float) * (size_t)(ceil_div(n, kTile) * n) + 255) & ~size_t(255);
-}
+size_t medoid_ws_bytes(int64_t n) { return medoid_ws_layout(n).bytes; }
 
 }  // namespace kvs

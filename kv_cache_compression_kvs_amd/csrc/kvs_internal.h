@@ -146,7 +146,7 @@ constexpr int64_t kSimRows = 1024;
 // Episode clustering limits: clusters per K-means and embedding width.
 constexpr int kMaxClusters = 16;
 constexpr int64_t kMaxEmbedDim = 2048;
-constexpr int64_t kMaxMedoidPoints = 64 * 65535;  // 64-point tiles, grid y below 2^16
+constexpr int64_t kMaxMedoidPoints = 32 * 65535;  // 32-point tiles, grid y below 2^16
 
 // Pass-1 tiling constants shared by the planner and the kernels.
 constexpr int kP1Rows = 256;      // query rows per pass-1 workgroup (4 waves x 64)

@@ -417,13 +417,13 @@ def test_episode_entry_points_reject_bad_arguments(K):
     assert km(wb=ws - 1) == 6
     assert km(x=FAKE + 4) == 5
     mw = K.kvs_medoids_workspace_bytes(10, 8, 2)
-    assert mw >= 10 * 4 and K.kvs_medoids_workspace_bytes(64 * 65535 + 1, 8, 2) == 0
+    assert mw >= 10 * 4 and K.kvs_medoids_workspace_bytes(32 * 65535 + 1, 8, 2) == 0
     assert h.kvs_medoids(FAKE, 10, 8, FAKE, 2, None, FAKE, FAKE, mw, None) == 1
     assert h.kvs_medoids(FAKE, 10, 8, FAKE, 2, FAKE, None, FAKE, mw, None) == 1
     assert h.kvs_medoids(FAKE, 10, 8, FAKE, 2, FAKE, FAKE, None, mw, None) == 1
     assert h.kvs_medoids(FAKE, 10, 8, FAKE, 2, FAKE, FAKE, FAKE, 4, None) == 6
     assert h.kvs_medoids(FAKE + 8, 10, 8, FAKE, 2, FAKE, FAKE, FAKE, mw, None) == 5
-    assert h.kvs_medoids(FAKE, 64 * 65535 + 1, 8, FAKE, 2, FAKE, FAKE, FAKE, 1 << 40, None) == 2
+    assert h.kvs_medoids(FAKE, 32 * 65535 + 1, 8, FAKE, 2, FAKE, FAKE, FAKE, 1 << 40, None) == 2
     assert h.kvs_match_episodes(FAKE, 10, 8, None, 2, FAKE, None) == 1
     assert h.kvs_match_episodes(FAKE, 10, 8, FAKE, 20, FAKE, None) == 2
     assert h.kvs_match_episodes(None, 0, 8, None, 2, None, None) == 0

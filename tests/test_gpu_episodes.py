@@ -112,6 +112,48 @@ def test_kmeans_zero_points_and_empty_clusters(K):
     assert abs(c[0, 0] - 0.05) < 1e-6 and abs(c[1, 0] - 10.1) < 1e-5
 
 
+def check_medoids(K, x, a, e):
+    n = len(a)
+    totals = torch.full((n,), float("nan"), device="cuda")
+    med = torch.full((e,), -9, dtype=torch.int32, device="cuda")
+    K.kvs_medoids(x.cuda(), a.cuda(), e, med, totals)
+    torch.cuda.synchronize()
+    x64, a64 = x.double().numpy(), a.numpy().astype(np.int64)
+    want_t = O.medoid_totals(x64, a64)
+    got_t = totals.cpu().double().numpy()
+    assert np.all(np.abs(got_t - want_t) <= REL * want_t + 1e-6)
+    want = O.medoids(x64, a64, e)
+    got = med.cpu().numpy()
+    for c in range(e):
+        if want[c] < 0:
+            assert got[c] == -1
+            continue
+        assert a64[got[c]] == c
+        best = want_t[want[c]]
+        assert want_t[got[c]] - best <= REL * best, (c, got[c], want[c])
+
+
+# Label layouts for the tile pairs the medoid kernel forms: clusters in
+# contiguous runs of the index order, one ragged point past a whole tile, one
+# cluster (every tile pair formed), many small clusters straddling tile edges,
+# and labels outside [0, e) (their points sum over their own label only).
+@pytest.mark.parametrize("layout,n,dim,e", [
+    ("runs", 700, 64, 3), ("ragged", 65, 8, 2), ("one", 300, 16, 1),
+    ("small", 1000, 32, 16), ("stray", 400, 24, 4), ("single", 1, 4, 2)])
+def test_medoids_label_layouts(K, layout, n, dim, e):
+    g = torch.Generator().manual_seed(7 * n + e)
+    x = torch.randn(n, dim, generator=g)
+    if layout == "runs":
+        a = torch.repeat_interleave(torch.arange(e), torch.tensor([250, 64, n - 314])).int()
+    elif layout == "stray":
+        a = torch.randint(0, e, (n,), generator=g).int()
+        a[::7] = -1
+        a[3::11] = e + 5
+    else:
+        a = torch.randint(0, e, (n,), generator=g).int()
+    check_medoids(K, x, a, e)
+
+
 @pytest.mark.parametrize("n,dim,e", [(1024, 1024, 4), (257, 2048, 3), (40, 12, 5)])
 def test_medoids_match_oracle(K, n, dim, e):
     g = torch.Generator().manual_seed(n)
