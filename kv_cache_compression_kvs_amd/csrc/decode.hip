@@ -14,13 +14,15 @@
 // 256-thread workgroup per split (split-K, so that a long head does not leave
 // the chip idle while short ones finish):
 //   decode_prefix  sp[u] = splits before unit u (one workgroup, ordered scan)
-//   decode_split   logits of the split's rows for a group of heads (each lane
-//                  owns one 16-byte piece of a row; the pieces of a row are
-//                  summed with DPP lane moves), per-head max and exp2 in LDS,
-//                  then the p-weighted sum of the V rows; writes (max, sum,
-//                  acc[d]) per head, max in the base-2 logit domain
+//   decode_split   one pass over the split's rows for a group of heads: each
+//                  lane owns one 16-byte piece of a row (the pieces of a row
+//                  are summed with DPP lane moves), K and V streamed together,
+//                  an online max / sum / p-weighted V sum per thread, merged
+//                  by log-sum-exp; writes (max, sum, acc[d]) per head, max in
+//                  the base-2 logit domain
 //   decode_merge   per (layer, head): log-sum-exp merge of its unit's splits
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 
 #include "kvs_device.h"
@@ -32,7 +34,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kHG = 4;  // heads per pass over a split's rows
+constexpr int kMaxHG = 4;  // most heads per pass over a split's rows
 
 struct DecodeArgs {
   const void* q;         // [L, Hq, D]
@@ -47,23 +49,6 @@ struct DecodeArgs {
   int32_t units, Hkv, Hq, G;
   float c1;              // log2(e) / sqrt(D)
 };
-
-__device__ __forceinline__ void load_piece(const float* p, float (&x)[4]) {
-  const float4 v = *reinterpret_cast<const float4*>(p);
-  x[0] = v.x;
-  x[1] = v.y;
-  x[2] = v.z;
-  x[3] = v.w;
-}
-
-__device__ __forceinline__ void load_piece(const __bf16* p, float (&x)[8]) {
-  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-}
 
 // Sum of x over the LPR consecutive lanes that hold one row's pieces (LPR in
 // {8, 16, 32}), left in every one of them.  Within a 16-lane row the partners
@@ -87,8 +72,6 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
 
 __global__ __launch_bounds__(1024) void decode_prefix(DecodeArgs a) {
   __shared__ int64_t wsum[16];
@@ -120,17 +103,40 @@ __global__ __launch_bounds__(1024) void decode_prefix(DecodeArgs a) {
   if (tid == 0) a.sp[a.units] = carry;
 }
 
-template <typename T, int D>
+// A row piece as 16 raw bytes, widened to fp32 where it is used.
+__device__ __forceinline__ u32x4 load_raw(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ void widen(const u32x4& w, float (&x)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(w[i]);
+}
+
+__device__ __forceinline__ void widen(const u32x4& w, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// One pass over the split's rows.  Each step the workgroup covers RPI rows
+// (a row's pieces on LPR consecutive lanes); the K and V pieces of U steps
+// are loaded together, so both streams are in flight at once.  Every thread
+// keeps, per head of the group, a running max m (base-2 logits), sum l and
+// accumulator acc of 2^(z - m) v over its rows, brought to the steps' max
+// once per U steps.  At the end the threads holding the same piece are
+// merged by log-sum-exp: across a wave's rows with lane shuffles, then across
+// the waves through LDS.  The partial (max, sum, acc) per head goes to
+// decode_merge.
+template <typename T, int D, int kHG>
 __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a) {
   constexpr int EPL = 16 / sizeof(T);      // elements per lane piece
   constexpr int LPR = D / EPL;             // lanes per row
-  constexpr int RPI = kThreads / LPR;      // rows per iteration of the workgroup
+  constexpr int RPI = kThreads / LPR;      // rows per step of the workgroup
   constexpr int ITERS = kDecodeRows / RPI;
-  static_assert(kDecodeRows % RPI == 0, "whole iterations");
-  constexpr int RPT = kDecodeRows / kThreads;   // rows per thread in the softmax step
-  static_assert(kDecodeRows % kThreads == 0, "whole rows per thread in the softmax step");
-  __shared__ float zs[kDecodeRows][kHG];
-  __shared__ float red[kWaves][kHG];
+  constexpr int U = 4;                     // steps whose loads are issued together
+  static_assert(kDecodeRows % RPI == 0 && ITERS % U == 0, "whole load groups");
+  __shared__ float red_m[kWaves][kHG], red_l[kWaves][kHG];
   __shared__ float racc[kWaves][kHG][D];
   __shared__ int32_t unit_sh;
 
@@ -154,113 +160,96 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a) {
   const int64_t l = u / a.Hkv, g = u % a.Hkv;
   const int piece = tid % LPR, rsub = tid / LPR;
   const T* qbase = static_cast<const T*>(a.q) + (l * a.Hq + g * a.G) * D + piece * EPL;
-  const T* kbase = static_cast<const T*>(a.k);
-  const T* vbase = static_cast<const T*>(a.v);
+  const T* kbase = static_cast<const T*>(a.k) + piece * EPL;
+  const T* vbase = static_cast<const T*>(a.v) + piece * EPL;
 
   for (int h0 = 0; h0 < a.G; h0 += kHG) {
     float qf[kHG][EPL];
 #pragma unroll
     for (int j = 0; j < kHG; ++j) {
       if (h0 + j < a.G) {
-        load_piece(qbase + (h0 + j) * D, qf[j]);
+        widen(load_raw(qbase + (h0 + j) * D), qf[j]);
       } else {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qf[j][e] = 0.f;
       }
     }
-    // logits of the split's rows
-#pragma unroll 4
-    for (int it = 0; it < ITERS; ++it) {
-      const int rloc = it * RPI + rsub;
-      const int64_t row = r0 + rloc;
-      float x[EPL];
-      load_piece(kbase + min(row, r1 - 1) * D + piece * EPL, x);
-      float z[kHG];
-#pragma unroll
-      for (int j = 0; j < kHG; ++j) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[j][e], x[e], acc);
-        z[j] = acc;
-      }
-#pragma unroll
-      for (int j = 0; j < kHG; ++j) z[j] = row_sum<LPR>(z[j]);
-      if (piece == 0) {
-#pragma unroll
-        for (int j = 0; j < kHG; ++j) zs[rloc][j] = row < r1 ? z[j] * a.c1 : -INFINITY;
-      }
-    }
-    __syncthreads();
-    // per-head max and sum over the split; thread t owns rows t + q * kThreads
-    float zt[RPT][kHG], mx[kHG], sm[kHG];
+    // finite start: a thread whose rows are all past the split's end keeps
+    // l = 0 and acc = 0, and every rescale factor stays finite
+    float m[kHG], lsum[kHG], acc[kHG][EPL];
 #pragma unroll
     for (int j = 0; j < kHG; ++j) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int q = 0; q < RPT; ++q) {
-        zt[q][j] = zs[tid + q * kThreads][j];
-        m = fmaxf(m, zt[q][j]);
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-      if (lane == 0) red[wave][j] = m;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kHG; ++j) {
-      mx[j] = red[0][j];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) mx[j] = fmaxf(mx[j], red[ww][j]);
-    }
-    __syncthreads();  // red is rewritten below
-#pragma unroll
-    for (int j = 0; j < kHG; ++j) {
-      float t = 0.f;
-#pragma unroll
-      for (int q = 0; q < RPT; ++q) {
-        const int r = tid + q * kThreads;
-        const float p = r < r1 - r0 ? exp2_hw(zt[q][j] - mx[j]) : 0.f;
-        zs[r][j] = p;
-        t += p;
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
-      if (lane == 0) red[wave][j] = t;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kHG; ++j) {
-      sm[j] = red[0][j];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) sm[j] += red[ww][j];
-    }
-    // p-weighted sum of the V rows
-    float acc[kHG][EPL];
-#pragma unroll
-    for (int j = 0; j < kHG; ++j) {
+      m[j] = -FLT_MAX;
+      lsum[j] = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[j][e] = 0.f;
     }
-#pragma unroll 4
-    for (int it = 0; it < ITERS; ++it) {
-      const int rloc = it * RPI + rsub;
-      const int64_t row = r0 + rloc;
-      float x[EPL];
-      load_piece(vbase + min(row, r1 - 1) * D + piece * EPL, x);
+    for (int it = 0; it < ITERS; it += U) {
+      u32x4 kr[U], vr[U];
+      bool ok[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int64_t row = r0 + (it + q) * RPI + rsub;
+        ok[q] = row < r1;
+        const int64_t rr = min(row, r1 - 1);
+        kr[q] = load_raw(kbase + rr * D);
+        vr[q] = load_raw(vbase + rr * D);
+      }
+      float z[U][kHG];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        float x[EPL];
+        widen(kr[q], x);
+#pragma unroll
+        for (int j = 0; j < kHG; ++j) {
+          float t = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) t = fmaf(qf[j][e], x[e], t);
+          z[q][j] = row_sum<LPR>(t);
+          z[q][j] = ok[q] ? z[q][j] * a.c1 : -INFINITY;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < kHG; ++j) {
-        const float p = zs[rloc][j];  // 0 past the split's end
+        float bm = z[0][j];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(p, x[e], acc[j][e]);
+        for (int q = 1; q < U; ++q) bm = fmaxf(bm, z[q][j]);
+        const float mn = fmaxf(m[j], bm);
+        const float sc = exp2_hw(m[j] - mn);
+        m[j] = mn;
+        lsum[j] *= sc;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] *= sc;
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        float x[EPL];
+        widen(vr[q], x);
+#pragma unroll
+        for (int j = 0; j < kHG; ++j) {
+          const float p = exp2_hw(z[q][j] - m[j]);  // 0 past the split's end
+          lsum[j] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(p, x[e], acc[j][e]);
+        }
       }
     }
-    // sum over the rows a wave holds (lanes with the same piece), then the waves
+    // merge the rows of a wave: lanes piece + k LPR hold the same piece
 #pragma unroll
     for (int off = LPR; off < 64; off <<= 1) {
 #pragma unroll
       for (int j = 0; j < kHG; ++j) {
+        const float mo = __shfl_xor(m[j], off, 64);
+        const float lo = __shfl_xor(lsum[j], off, 64);
+        const float mn = fmaxf(m[j], mo);
+        const float s1 = exp2_hw(m[j] - mn), s2 = exp2_hw(mo - mn);
+        m[j] = mn;
+        lsum[j] = lsum[j] * s1 + lo * s2;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[j][e] += __shfl_xor(acc[j][e], off, 64);
+        for (int e = 0; e < EPL; ++e) {
+          const float ao = __shfl_xor(acc[j][e], off, 64);
+          acc[j][e] = acc[j][e] * s1 + ao * s2;
+        }
       }
     }
     if (lane < LPR) {
@@ -268,23 +257,37 @@ __global__ __launch_bounds__(kThreads) void decode_split(DecodeArgs a) {
       for (int j = 0; j < kHG; ++j) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) racc[wave][j][piece * EPL + e] = acc[j][e];
+        if (lane == 0) {
+          red_m[wave][j] = m[j];
+          red_l[wave][j] = lsum[j];
+        }
       }
     }
     __syncthreads();
+    // merge the waves
     for (int i = tid; i < kHG * D; i += kThreads) {
       const int j = i / D, e = i % D;
       if (h0 + j < a.G) {
-        float t = racc[0][j][e];
+        float M = red_m[0][j];
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) t += racc[ww][j][e];
+        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww][j]);
+        float t = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) t += racc[ww][j][e] * exp2_hw(red_m[ww][j] - M);
         a.part_acc[(w * a.G + h0 + j) * D + e] = t;
       }
     }
     if (tid < kHG && h0 + tid < a.G) {
-      a.part_ml[(w * a.G + h0 + tid) * 2] = mx[tid];
-      a.part_ml[(w * a.G + h0 + tid) * 2 + 1] = sm[tid];
+      float M = red_m[0][tid];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww][tid]);
+      float L = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) L += red_l[ww][tid] * exp2_hw(red_m[ww][tid] - M);
+      a.part_ml[(w * a.G + h0 + tid) * 2] = M;
+      a.part_ml[(w * a.G + h0 + tid) * 2 + 1] = L;
     }
-    __syncthreads();  // zs, red and racc are reused by the next head group
+    __syncthreads();  // red_m, red_l and racc are reused by the next head group
   }
 }
 
@@ -295,9 +298,12 @@ __global__ __launch_bounds__(D) void decode_merge(DecodeArgs a) {
   const int64_t u = l * a.Hkv + h / a.G, j = h % a.G;
   const int e = threadIdx.x;
   const int64_t s0 = min(a.sp[u], a.slots), s1 = min(a.sp[u + 1], a.slots);
+  // both loops unrolled so that several splits' loads are in flight
   float m = -INFINITY;
+#pragma unroll 4
   for (int64_t s = s0; s < s1; ++s) m = fmaxf(m, a.part_ml[(s * a.G + j) * 2]);
   float den = 0.f, num = 0.f;
+#pragma unroll 4
   for (int64_t s = s0; s < s1; ++s) {
     const float f = exp2_hw(a.part_ml[(s * a.G + j) * 2] - m);
     den = fmaf(a.part_ml[(s * a.G + j) * 2 + 1], f, den);
@@ -313,8 +319,16 @@ int decode_run(DecodeArgs a, int64_t n_heads, hipStream_t st) {
     hipLaunchKernelGGL(decode_prefix, dim3(1), dim3(1024), 0, st, a);
   }
   if (a.slots > 0) {
+    // heads per pass: the whole group when it has at most kMaxHG heads (no
+    // idle registers), else passes of kMaxHG
     TraceScope ts("decode_split", st);
-    hipLaunchKernelGGL((decode_split<T, D>), dim3((unsigned)a.slots), dim3(kThreads), 0, st, a);
+    const dim3 grid((unsigned)a.slots), block(kThreads);
+    switch (std::min(a.G, kMaxHG)) {
+      case 1: hipLaunchKernelGGL((decode_split<T, D, 1>), grid, block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((decode_split<T, D, 2>), grid, block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((decode_split<T, D, 3>), grid, block, 0, st, a); break;
+      default: hipLaunchKernelGGL((decode_split<T, D, kMaxHG>), grid, block, 0, st, a); break;
+    }
   }
   TraceScope ts("decode_merge", st);
   hipLaunchKernelGGL(decode_merge<D>, dim3((unsigned)n_heads), dim3(D), 0, st, a);
