@@ -147,6 +147,9 @@ DECODE = [
     (1, 4, 4, 128, torch.bfloat16, [5, 0, 0, 300]),         # G = 1, empty heads
     (1, 6, 2, 64, torch.float32, [300, 17]),
     (2, 12, 3, 128, torch.float32, [100, 400, 256, 1, 2, 999]),
+    (1, 6, 3, 128, torch.bfloat16, [1024, 3, 700]),        # G = 2: two heads per pass
+    (1, 10, 2, 64, torch.bfloat16, [2049, 511]),           # G = 5: passes of 4 and 1 heads
+    (1, 12, 2, 128, torch.float32, [513, 1536]),           # G = 6: passes of 4 and 2 heads
 ]
 
 
