@@ -164,7 +164,8 @@ int kvs_select(const kvs_problem* p, const float* scores, const int64_t* k_per_l
  * k_out, v_out: device.  out_row_stride == 0: packed like kept (row
  * Hkv * sum_{l'<l} k_l' + g * k_l + t).  out_row_stride > 0: slab (l, g)
  * starts at row (l * Hkv + g) * out_row_stride (needs k_l <= out_row_stride).
- * The outputs must not overlap K or V.
+ * The outputs must not overlap K or V.  Either k_out or v_out (not both) may
+ * be NULL: that tensor is not compacted and its input may be NULL as well.
  */
 int kvs_compact(const kvs_problem* p, const void* k, const void* v, const int32_t* kept,
                 const int64_t* k_per_layer, void* k_out, void* v_out,
@@ -178,6 +179,9 @@ int kvs_compact(const kvs_problem* p, const void* k, const void* v, const int32_
  * total_budget >= L * N every position is kept (the cache is copied through
  * and scores are still written).  scores, kept, k_out, v_out, out_row_stride
  * and ws are as in the calls above; kept needs Hkv * sum_l k_l entries.
+ * v_out may be NULL: V is then neither read nor compacted, for a caller that
+ * compacts it apart with kvs_compact or kvs_compact_seg (for example on a
+ * second stream, beside the next step's scoring, which reads only K).
  */
 int kvs_compress_block(const kvs_problem* p, const void* q, const void* k, const void* v,
                        int64_t total_budget, const double* sens, double alpha,
@@ -224,6 +228,19 @@ int kvs_compress_block_seg(const kvs_problem* p, const void* q, const kvs_kv_seg
                            float* scores, int32_t* kept, void* k_out, void* v_out,
                            int64_t out_row_stride, int64_t* k_per_layer_out,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kvs_compact on a cache given as two segments (kvs_kv_segments, with the
+ * constraints of kvs_compress_block_seg): the headwise compaction (KV²
+ * summary, "전제와 한계") of the concatenated cache, bit for bit.  kept,
+ * k_per_layer, out_row_stride and the NULL rules for k_out / v_out are those
+ * of kvs_compact; only the segments' pointers of a compacted tensor are read.
+ * Errors: as kvs_compact, and KVS_E_NULL for seg == NULL, KVS_E_SHAPE for
+ * invalid segments.
+ */
+int kvs_compact_seg(const kvs_problem* p, const kvs_kv_segments* seg, const int32_t* kept,
+                    const int64_t* k_per_layer, void* k_out, void* v_out,
+                    int64_t out_row_stride, void* stream);
 
 /*
  * Stage-1 query selection (KV² summary, "어떻게 동작하나"), also the selection

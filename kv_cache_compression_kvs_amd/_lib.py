@@ -72,6 +72,8 @@ SIGNATURES = {
                                          ctypes.POINTER(KvsKvSegments), c_int64, P_F64, c_double,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_int64, P_I64,
                                          c_void_p, c_size_t, c_void_p]),
+    "kvs_compact_seg": (c_int32, [ctypes.POINTER(KvsProblem), ctypes.POINTER(KvsKvSegments),
+                                  c_void_p, P_I64, c_void_p, c_void_p, c_int64, c_void_p]),
     "kvs_query_workspace_bytes": (c_size_t, [ctypes.POINTER(KvsProblem)]),
     "kvs_query_counts": (c_int32, [ctypes.POINTER(KvsProblem), c_double, P_I64, P_I64]),
     "kvs_query_select": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p, c_double, c_void_p,

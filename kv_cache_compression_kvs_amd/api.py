@@ -190,6 +190,21 @@ def kvs_compress_block_seg(p: KvsProblem, q: Tensorish, k_head: Tensorish, v_hea
     return np.array(kl[:], dtype=np.int64)
 
 
+def kvs_compact_seg(p: KvsProblem, k_head: Tensorish, v_head: Tensorish, head_rows: int,
+                    head_row_stride: int, k_tail: Tensorish, v_tail: Tensorish, tail_row0: int,
+                    tail_row_stride: int, kept: Tensorish, k_per_layer: Sequence[int],
+                    k_out: Tensorish, v_out: Tensorish, out_row_stride: int = 0,
+                    stream=None) -> None:
+    """kvs_compact on a cache held as two segments; k_out or v_out may be None."""
+    seg = _lib.KvsKvSegments(_dev(k_head, "k_head"), _dev(v_head, "v_head"), head_rows,
+                             head_row_stride, _dev(k_tail, "k_tail"), _dev(v_tail, "v_tail"),
+                             tail_row0, tail_row_stride)
+    _check(_lib.lib().kvs_compact_seg(ctypes.byref(p), ctypes.byref(seg), _dev(kept, "kept"),
+                                      _i64(k_per_layer), _dev(k_out, "k_out"),
+                                      _dev(v_out, "v_out"), out_row_stride, _stream(stream)),
+           "kvs_compact_seg")
+
+
 def kvs_query_workspace_bytes(p: KvsProblem) -> int:
     return int(_lib.lib().kvs_query_workspace_bytes(ctypes.byref(p)))
 

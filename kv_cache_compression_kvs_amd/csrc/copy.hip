@@ -34,7 +34,9 @@ struct CompactArgs {
   LayerTable t;
 };
 
-template <int LPR>
+// PLANES: bit 0 moves K, bit 1 moves V (a caller may compact the two apart,
+// e.g. V on a second stream while the next step scores with K).
+template <int LPR, int PLANES>
 __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   constexpr int RPP = kThreads / LPR;
   const int64_t unit = blockIdx.y;
@@ -47,8 +49,8 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
   const int64_t hoff = slab * a.h_stride * a.row_bytes;
   const int64_t toff = (slab * a.t_stride + a.t_row0 - a.split) * a.row_bytes;  // + i * row_bytes
   const int64_t orow0 = a.out_stride ? (l * a.Hkv + g) * a.out_stride : a.t.off[l] + g * kl;
-  uint8_t* ko = a.ko + orow0 * a.row_bytes;
-  uint8_t* vo = a.vo + orow0 * a.row_bytes;
+  uint8_t* ko = (PLANES & 1) ? a.ko + orow0 * a.row_bytes : nullptr;
+  uint8_t* vo = (PLANES & 2) ? a.vo + orow0 * a.row_bytes : nullptr;
   const int piece = threadIdx.x % LPR;
   const int rsub = threadIdx.x / LPR;
 
@@ -65,16 +67,16 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     const int64_t i = ok[u] ? idx[u] : 0;
     const bool head = i < a.split;
     const int64_t src = (head ? hoff : toff) + i * a.row_bytes + piece * 16;
-    kb[u] = __builtin_nontemporal_load((const u32x4*)((head ? a.kh : a.kt) + src));
-    vb[u] = __builtin_nontemporal_load((const u32x4*)((head ? a.vh : a.vt) + src));
+    if (PLANES & 1) kb[u] = __builtin_nontemporal_load((const u32x4*)((head ? a.kh : a.kt) + src));
+    if (PLANES & 2) vb[u] = __builtin_nontemporal_load((const u32x4*)((head ? a.vh : a.vt) + src));
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t t = t0 + u * RPP + rsub;
     if (ok[u]) {
       const int64_t dst = t * a.row_bytes + piece * 16;
-      __builtin_nontemporal_store(kb[u], (u32x4*)(ko + dst));
-      __builtin_nontemporal_store(vb[u], (u32x4*)(vo + dst));
+      if (PLANES & 1) __builtin_nontemporal_store(kb[u], (u32x4*)(ko + dst));
+      if (PLANES & 2) __builtin_nontemporal_store(vb[u], (u32x4*)(vo + dst));
     }
   }
 }
@@ -185,10 +187,12 @@ template <int LPR>
 int compact_lpr(const CompactArgs& a, int64_t units, int32_t k_max, hipStream_t st) {
   constexpr int RPP = kThreads / LPR;
   const int64_t gx = ceil_div(k_max, RPP * kUnroll);
-  if (gx <= 0 || units <= 0) return 0;
+  if (gx <= 0 || units <= 0 || (!a.ko && !a.vo)) return 0;
   TraceScope ts("compact", st);
-  hipLaunchKernelGGL(compact_kernel<LPR>, dim3((unsigned)gx, (unsigned)units), dim3(kThreads), 0,
-                     st, a);
+  const dim3 grid((unsigned)gx, (unsigned)units), block(kThreads);
+  if (a.ko && a.vo) hipLaunchKernelGGL((compact_kernel<LPR, 3>), grid, block, 0, st, a);
+  else if (a.ko) hipLaunchKernelGGL((compact_kernel<LPR, 1>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((compact_kernel<LPR, 2>), grid, block, 0, st, a);
   return (int)hipGetLastError();
 }
 

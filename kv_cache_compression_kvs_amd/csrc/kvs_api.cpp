@@ -134,13 +134,40 @@ KvSrc single_src(const kvs_problem& p, const void* k, const void* v) {
   return kv;
 }
 
-// Null and alignment checks of the buffers a call reads (V only if need_v).
-int check_src(const kvs_problem& p, const KvSrc& kv, bool need_v) {
+// Shape checks of a two-segment cache (kvs_kv_segments) against p.
+int check_segments(const kvs_problem& p, const kvs_kv_segments& seg) {
+  const int64_t N = p.n_cache;
+  const int64_t h = seg.head_rows;
+  if (p.kv_row_stride != 0) return KVS_E_SHAPE;  // strides come with the segments
+  if (h < 0 || h > N || (h % 8 != 0 && h != N)) return KVS_E_SHAPE;
+  if (h > 0 && seg.head_row_stride < h) return KVS_E_SHAPE;
+  if (h < N && (seg.tail_row0 < 0 || seg.tail_row_stride < seg.tail_row0 + (N - h)))
+    return KVS_E_SHAPE;
+  return KVS_OK;
+}
+
+KvSrc segment_src(const kvs_kv_segments& seg) {
+  KvSrc kv;
+  kv.k_head = seg.k_head;
+  kv.v_head = seg.v_head;
+  kv.head_stride = seg.head_row_stride;
+  kv.k_tail = seg.k_tail;
+  kv.v_tail = seg.v_tail;
+  kv.tail_stride = seg.tail_row_stride;
+  kv.tail_row0 = seg.tail_row0;
+  kv.split = seg.head_rows;
+  return kv;
+}
+
+// Null and alignment checks of the buffers a call reads (K if need_k, V if
+// need_v).
+int check_src(const kvs_problem& p, const KvSrc& kv, bool need_k, bool need_v) {
   if (p.n_cache == 0) return KVS_OK;
   const bool head = kv.split > 0, tail = kv.split < p.n_cache;
-  if ((head && !kv.k_head) || (tail && !kv.k_tail)) return KVS_E_NULL;
+  if (need_k && ((head && !kv.k_head) || (tail && !kv.k_tail))) return KVS_E_NULL;
   if (need_v && ((head && !kv.v_head) || (tail && !kv.v_tail))) return KVS_E_NULL;
-  if ((head && !aligned(kv.k_head, 16)) || (tail && !aligned(kv.k_tail, 16))) return KVS_E_ALIGN;
+  if (need_k && ((head && !aligned(kv.k_head, 16)) || (tail && !aligned(kv.k_tail, 16))))
+    return KVS_E_ALIGN;
   if (need_v && ((head && !aligned(kv.v_head, 16)) || (tail && !aligned(kv.v_tail, 16))))
     return KVS_E_ALIGN;
   return KVS_OK;
@@ -150,7 +177,7 @@ int do_score(const kvs_problem& p, const void* q, const KvSrc& kv, float* scores
              size_t ws_bytes) {
   const ScorePlan pl = plan_score(p);
   if (p.n_cache > 0 && !scores) return KVS_E_NULL;
-  if (int st = check_src(p, kv, false)) return st;
+  if (int st = check_src(p, kv, true, false)) return st;
   if (pl.n_queries > 0 && !q) return KVS_E_NULL;
   if (pl.ws_bytes > 0 && !ws) return KVS_E_NULL;
   if (ws_bytes < pl.ws_bytes) return KVS_E_WORKSPACE;
@@ -209,8 +236,8 @@ int compress(const kvs_problem& p, const void* q, const KvSrc& kv, int64_t total
   st = do_score(p, q, kv, scores, ws, ws_bytes);
   if (st) return st;
   if ((st = check_select_ws(p, ws, ws_bytes))) return st;
-  if ((st = check_src(p, kv, true))) return st;
-  if (p.n_cache > 0 && (!kept || !k_out || !v_out)) return KVS_E_NULL;
+  if ((st = check_src(p, kv, true, v_out != nullptr))) return st;
+  if (p.n_cache > 0 && (!kept || !k_out)) return KVS_E_NULL;
   if ((kept && !aligned(kept, 4)) || (k_out && !aligned(k_out, 16)) ||
       (v_out && !aligned(v_out, 16)))
     return KVS_E_ALIGN;
@@ -364,12 +391,33 @@ int kvs_compact(const kvs_problem* p, const void* k, const void* v, const int32_
   st = build_table(*p, k_per_layer, false, out_row_stride, &t, &kmax);
   if (st) return st;
   if (kmax == 0) return KVS_OK;
-  if (!k || !v || !kept || !k_out || !v_out) return KVS_E_NULL;
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
-      !aligned(kept, 4))
+  if (!kept || (!k_out && !v_out) || (k_out && !k) || (v_out && !v)) return KVS_E_NULL;
+  if ((k_out && (!aligned(k, 16) || !aligned(k_out, 16))) ||
+      (v_out && (!aligned(v, 16) || !aligned(v_out, 16))) || !aligned(kept, 4))
     return KVS_E_ALIGN;
   return to_status(launch_compact(*p, single_src(*p, k, v), kept, t, kmax, k_out, v_out,
                                   out_row_stride, stream));
+}
+
+int kvs_compact_seg(const kvs_problem* p, const kvs_kv_segments* seg, const int32_t* kept,
+                    const int64_t* k_per_layer, void* k_out, void* v_out, int64_t out_row_stride,
+                    void* stream) {
+  int st = check(p);
+  if (st) return st;
+  if (!seg) return KVS_E_NULL;
+  if ((st = check_segments(*p, *seg))) return st;
+  if (out_row_stride < 0) return KVS_E_SHAPE;
+  LayerTable t;
+  int32_t kmax = 0;
+  st = build_table(*p, k_per_layer, false, out_row_stride, &t, &kmax);
+  if (st) return st;
+  if (kmax == 0) return KVS_OK;
+  const KvSrc kv = segment_src(*seg);
+  if (!kept || (!k_out && !v_out)) return KVS_E_NULL;
+  if ((st = check_src(*p, kv, k_out != nullptr, v_out != nullptr))) return st;
+  if ((k_out && !aligned(k_out, 16)) || (v_out && !aligned(v_out, 16)) || !aligned(kept, 4))
+    return KVS_E_ALIGN;
+  return to_status(launch_compact(*p, kv, kept, t, kmax, k_out, v_out, out_row_stride, stream));
 }
 
 int kvs_compress_block(const kvs_problem* p, const void* q, const void* k, const void* v,
@@ -390,24 +438,9 @@ int kvs_compress_block_seg(const kvs_problem* p, const void* q, const kvs_kv_seg
   int st = check(p);
   if (st) return st;
   if (!seg) return KVS_E_NULL;
-  const int64_t N = p->n_cache;
-  const int64_t h = seg->head_rows;
-  if (p->kv_row_stride != 0) return KVS_E_SHAPE;  // strides come with the segments
-  if (h < 0 || h > N || (h % 8 != 0 && h != N)) return KVS_E_SHAPE;
-  if (h > 0 && seg->head_row_stride < h) return KVS_E_SHAPE;
-  if (h < N && (seg->tail_row0 < 0 || seg->tail_row_stride < seg->tail_row0 + (N - h)))
-    return KVS_E_SHAPE;
-  KvSrc kv;
-  kv.k_head = seg->k_head;
-  kv.v_head = seg->v_head;
-  kv.head_stride = seg->head_row_stride;
-  kv.k_tail = seg->k_tail;
-  kv.v_tail = seg->v_tail;
-  kv.tail_stride = seg->tail_row_stride;
-  kv.tail_row0 = seg->tail_row0;
-  kv.split = h;
-  return compress(*p, q, kv, total_budget, sens, alpha, scores, kept, k_out, v_out,
-                  out_row_stride, k_per_layer_out, ws, ws_bytes, stream);
+  if ((st = check_segments(*p, *seg))) return st;
+  return compress(*p, q, segment_src(*seg), total_budget, sens, alpha, scores, kept,
+                  k_out, v_out, out_row_stride, k_per_layer_out, ws, ws_bytes, stream);
 }
 
 size_t kvs_query_workspace_bytes(const kvs_problem* p) {
@@ -486,7 +519,7 @@ int kvs_compress_global(const kvs_problem* p, const void* q, const void* k, cons
   if ((st = check_global(*p, total_budget))) return st;
   const KvSrc kv = single_src(*p, k, v);
   if ((st = do_score(*p, q, kv, scores, ws, ws_bytes))) return st;
-  if ((st = check_src(*p, kv, true))) return st;
+  if ((st = check_src(*p, kv, true, true))) return st;
   if (!offsets || !ws) return KVS_E_NULL;
   if (total_budget > 0 && (!kept || !k_out || !v_out)) return KVS_E_NULL;
   if (ws_bytes < select_ws_layout(*p).bytes) return KVS_E_WORKSPACE;

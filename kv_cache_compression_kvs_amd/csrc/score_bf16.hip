@@ -142,10 +142,15 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
                                                  (int)(uint32_t)((rf - a.split) * ROWB), 0, 0);
     }
   };
+  // Fragment (kb, ks) of a tile: row kb*32 + col, chunk 2ks + half.  As
+  // 32 % CPR == 0 the row's swizzle is col % CPR, and the chunk's byte offset
+  // (2ks ^ half ^ (col % CPR)) * 16 splits into (16 (half ^ (col % CPR))) ^ 32ks
+  // below ROWB: one per-lane base XORed with a constant per ks, so the
+  // fragment addresses take no registers of their own.
+  static_assert(32 % CPR == 0, "a 32-row block starts on a swizzle period");
+  const uint32_t fbase = (uint32_t)(col * ROWB + ((half ^ (col & (CPR - 1))) * 16));
   auto afrag = [&](const uint8_t* buf, int kb, int ks) __attribute__((always_inline)) -> bf16x8 {
-    const int row = kb * 32 + col;
-    const int c = 2 * ks + half;
-    return *(const bf16x8*)(buf + row * ROWB + ((c ^ (row & (CPR - 1))) * 16));
+    return *(const bf16x8*)(buf + kb * 32 * ROWB + (fbase ^ (uint32_t)(32 * ks)));
   };
 
   // Exact update by one block: move m to the block's max if larger, rescale
@@ -258,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
     }
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    const int64_t valid = nkeys - u * TK;
+    const int valid = (int)min(nkeys - u * TK, (int64_t)TK);  // keys of this tile
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) {
       if (kb * 32 < valid) {

@@ -10,7 +10,9 @@ BlockLoop   EpiCache review ("[26'ICML] EpiCache"), "방법: 3단계" (2) and
             copied behind the cache first, and so are the blocks before the
             first compression: until then the cache is the leading rows of
             the token buffer, copied into a cache buffer only if it is asked
-            for before any compression.
+            for before any compression.  Scoring reads only K, so with
+            overlap_v each compression gathers K on the caller's stream and V
+            on a second stream, where it overlaps the next step's scoring.
 episodic    EpiCache review, "방법: 3단계" (2) and Fig. 3(b), with the
             "+α: 레이어별 예산 배분" budget split: one compressed cache per
             episode, built from that episode's prompt queries.
@@ -32,7 +34,7 @@ class BlockLoop:
 
     def __init__(self, layers: int, q_heads: int, kv_heads: int, head_dim: int,
                  dtype: torch.dtype, block_len: int, budget_m: int, n_sinks: int,
-                 q_per_step: int, device="cuda"):
+                 q_per_step: int, device="cuda", overlap_v: bool = False):
         self.L, self.Hq, self.Hkv, self.d = layers, q_heads, kv_heads, head_dim
         self.dtype = dtype
         self.B, self.M, self.S, self.nq = block_len, budget_m, n_sinks, q_per_step
@@ -41,7 +43,15 @@ class BlockLoop:
         self.k = [torch.empty(shape, dtype=dtype, device=device) for _ in range(2)]
         self.v = [torch.empty(shape, dtype=dtype, device=device) for _ in range(2)]
         self.scores = torch.empty(layers * kv_heads * self.cap, dtype=torch.float32, device=device)
-        self.kept = torch.empty(layers * kv_heads * budget_m, dtype=torch.int32, device=device)
+        # Two kept lists: the V gather of step b (second stream) still reads
+        # one while step b + 1 selects into the other.
+        self._kept = [torch.empty(layers * kv_heads * budget_m, dtype=torch.int32, device=device)
+                      for _ in range(2)]
+        self._kept_free: List[Optional[torch.cuda.Event]] = [None, None]
+        self._ki = 0
+        self.kept = self._kept[0]        # the latest compression's kept positions
+        self.side = torch.cuda.Stream(device=device) if overlap_v else None
+        self._v_done: Optional[torch.cuda.Event] = None
         self.ws = api.workspace(self.problem(self.cap), device)
         self.reset()
 
@@ -55,14 +65,47 @@ class BlockLoop:
                                 self.dtype, kv_row_stride=stride)
 
     def reset(self) -> None:
+        self.join()
         self.cur = 0
         self.n = 0
         self._tok = None   # (k_tokens, v_tokens) while the cache is their rows [0, n)
+
+    def join(self) -> None:
+        """Makes the caller's stream wait for the V gathers in flight."""
+        if self._v_done is not None:
+            torch.cuda.current_stream().wait_event(self._v_done)
+            self._v_done = None
+
+    def _compress(self, compress_k: Callable, gather_v: Callable, nxt: int) -> None:
+        """One compression: compress_k(kept, v_out) scores, selects and gathers
+        K (and V when v_out is given) on the caller's stream and returns the
+        per-layer budgets; gather_v(kept, budgets) gathers V."""
+        i = self._ki
+        self._ki ^= 1
+        kept = self._kept[i]
+        main = torch.cuda.current_stream()
+        if self._kept_free[i] is not None:   # the V gather that last read this list
+            main.wait_event(self._kept_free[i])
+        if self.side is None:
+            compress_k(kept, self.v[nxt])
+        else:
+            kl = compress_k(kept, None)
+            ready = torch.cuda.Event()
+            ready.record(main)
+            with torch.cuda.stream(self.side):
+                self.side.wait_event(ready)
+                gather_v(kept, kl)
+                done = torch.cuda.Event()
+                done.record(self.side)
+            self._kept_free[i] = done
+            self._v_done = done
+        self.kept = kept
 
     def _materialize(self) -> None:
         """Copies a cache still held as token rows [0, n) into the cache buffer."""
         if self._tok is None:
             return
+        self.join()
         kt, vt = self._tok
         self._tok = None
         if self.n:
@@ -74,6 +117,7 @@ class BlockLoop:
 
     def load_cache(self, k: torch.Tensor, v: torch.Tensor, n: int) -> None:
         """Sets the cache to the first n rows of k, v [L, Hkv, >= n, d]."""
+        self.join()
         self._tok = None
         self.cur = 0
         self.n = n
@@ -105,22 +149,33 @@ class BlockLoop:
                 self.n += nb
                 return False
             p = self.problem(self.n + nb, row_stride=T)
-            api.kvs_compress_block(p, q_step, k_tokens, v_tokens, self.M * self.L, None, 0.0,
-                                   self.scores, self.kept, self.k[nxt], self.v[nxt],
-                                   out_row_stride=self.cap, ws=self.ws)
+            self._compress(
+                lambda kept, v_out: api.kvs_compress_block(
+                    p, q_step, k_tokens, v_tokens, self.M * self.L, None, 0.0, self.scores,
+                    kept, self.k[nxt], v_out, out_row_stride=self.cap, ws=self.ws),
+                lambda kept, kl: api.kvs_compact(p, None, v_tokens, kept, kl, None, self.v[nxt],
+                                                 out_row_stride=self.cap),
+                nxt)
             self._tok = None
             self.cur = nxt
             self.n = self.M
             return True
         if self.n + nb > self.M and self.n % 8 == 0:
             p = self.problem(self.n + nb, row_stride=0)
-            api.kvs_compress_block_seg(p, q_step, self.k[self.cur], self.v[self.cur], self.n,
-                                       self.cap, k_tokens, v_tokens, r0, T, self.M * self.L,
-                                       None, 0.0, self.scores, self.kept, self.k[nxt],
-                                       self.v[nxt], out_row_stride=self.cap, ws=self.ws)
+            cur, n = self.cur, self.n
+            self._compress(
+                lambda kept, v_out: api.kvs_compress_block_seg(
+                    p, q_step, self.k[cur], self.v[cur], n, self.cap, k_tokens, v_tokens, r0, T,
+                    self.M * self.L, None, 0.0, self.scores, kept, self.k[nxt], v_out,
+                    out_row_stride=self.cap, ws=self.ws),
+                lambda kept, kl: api.kvs_compact_seg(
+                    p, None, self.v[cur], n, self.cap, None, v_tokens, r0, T, kept, kl, None,
+                    self.v[nxt], out_row_stride=self.cap),
+                nxt)
             self.cur = nxt
             self.n = self.M
             return True
+        self.join()   # the V buffer may still be written by the last V gather
         api.kvs_append_rows(slabs, self.d, self.dtype, k_tokens, T, r0, nb,
                             self.k[self.cur], self.cap, self.n)
         api.kvs_append_rows(slabs, self.d, self.dtype, v_tokens, T, r0, nb,
@@ -129,9 +184,14 @@ class BlockLoop:
         if self.n <= self.M:
             return False
         p = self.problem(self.n)
-        api.kvs_compress_block(p, q_step, self.k[self.cur], self.v[self.cur],
-                               self.M * self.L, None, 0.0, self.scores, self.kept,
-                               self.k[nxt], self.v[nxt], out_row_stride=self.cap, ws=self.ws)
+        cur = self.cur
+        self._compress(
+            lambda kept, v_out: api.kvs_compress_block(
+                p, q_step, self.k[cur], self.v[cur], self.M * self.L, None, 0.0, self.scores,
+                kept, self.k[nxt], v_out, out_row_stride=self.cap, ws=self.ws),
+            lambda kept, kl: api.kvs_compact(p, None, self.v[cur], kept, kl, None, self.v[nxt],
+                                             out_row_stride=self.cap),
+            nxt)
         self.cur = nxt
         self.n = self.M
         return True
@@ -146,17 +206,20 @@ class BlockLoop:
             scored += int(did)
             if on_step is not None:
                 on_step(b, self, did)
+        self.join()
         return scored
 
     def cache_view(self):
         """The current cache (k, v) [L, Hkv, n, d] where it lies: the cache
         buffer, or the token buffer's leading rows before any compression."""
+        self.join()
         if self._tok is not None:
             return self._tok[0][:, :, :self.n], self._tok[1][:, :, :self.n]
         return self.k[self.cur][:, :, :self.n], self.v[self.cur][:, :, :self.n]
 
     def cache(self):
         """Views of the current cache in the cache buffer: (k, v) [L, Hkv, n, d]."""
+        self.join()
         self._materialize()
         return self.k[self.cur][:, :, :self.n], self.v[self.cur][:, :, :self.n]
 

@@ -181,6 +181,95 @@ def test_select_nan_orders_above_inf(K, N):
     assert np.array_equal(kept.cpu().numpy(), want)
 
 
+def test_compact_seg_planes_match_one_gather(K):
+    """kvs_compact_seg of K alone and of V alone equals a gather of the
+    concatenated cache, bit for bit, and an index outside the cache leaves its
+    output row as it was."""
+    L, Hkv, d, h, N, cap = 2, 3, 128, 40, 72, 64
+    g = torch.Generator().manual_seed(11)
+    kh = torch.randn(L, Hkv, cap, d, generator=g).bfloat16()
+    vh = torch.randn(L, Hkv, cap, d, generator=g).bfloat16()
+    T = 100
+    kt = torch.randn(L, Hkv, T, d, generator=g).bfloat16()
+    vt = torch.randn(L, Hkv, T, d, generator=g).bfloat16()
+    r0 = 50                                   # tail rows [r0, r0 + N - h) of the token buffer
+    kcat = torch.cat([kh[:, :, :h], kt[:, :, r0:r0 + N - h]], dim=2)
+    vcat = torch.cat([vh[:, :, :h], vt[:, :, r0:r0 + N - h]], dim=2)
+    kl = [20, 20]
+    kept = torch.stack([torch.sort(torch.randperm(N, generator=g)[:20]).values
+                        for _ in range(L * Hkv)]).int()
+    kept[1, 3] = N + 7                         # outside the cache: skipped
+    p = K.make_problem(L, 2 * Hkv, Hkv, d, N, 4, N - 4, 1, torch.bfloat16, kv_row_stride=0)
+    want_k = torch.gather(kcat.view(L * Hkv, N, d), 1,
+                          kept.long().clamp(max=N - 1)[:, :, None].expand(-1, -1, d))
+    want_v = torch.gather(vcat.view(L * Hkv, N, d), 1,
+                          kept.long().clamp(max=N - 1)[:, :, None].expand(-1, -1, d))
+    for planes in ("k", "v"):
+        ko = torch.full((L, Hkv, cap, d), 7.0).bfloat16().cuda()
+        vo = torch.full((L, Hkv, cap, d), 7.0).bfloat16().cuda()
+        K.kvs_compact_seg(p, kh.cuda() if planes == "k" else None, vh.cuda() if planes == "v" else None,
+                          h, cap, kt.cuda() if planes == "k" else None,
+                          vt.cuda() if planes == "v" else None, r0, T, kept.cuda(), kl,
+                          ko if planes == "k" else None, vo if planes == "v" else None,
+                          out_row_stride=cap)
+        torch.cuda.synchronize()
+        got = (ko if planes == "k" else vo).cpu().view(L * Hkv, cap, d)[:, :20]
+        untouched = (vo if planes == "k" else ko).cpu()
+        want = (want_k if planes == "k" else want_v).clone()
+        want[1, 3] = 7.0
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), planes
+        assert torch.all(untouched == 7.0), planes
+
+
+@pytest.mark.parametrize("case", ["full", "ragged", "loaded"])
+def test_block_loop_v_on_second_stream_matches_one_stream(K, case):
+    """V gathered on a second stream, beside the next step's scoring, gives the
+    same scores and kept lists at every step and the same final cache, bit for
+    bit, as K and V gathered together on one stream.  Covers the in-place first
+    compression, the two-segment compressions, a ragged last block and (a cache
+    of M - 5 rows loaded first) the appended-block path.  Nothing joins the two
+    streams between steps, so the gathers really overlap the scoring."""
+    from kv_cache_compression_kvs_amd import drivers
+    w = SMALL["epicache_block_loop"]
+    s = w.shape
+    x = gen.block_loop_inputs(w)
+    T = 1100 if case == "ragged" else x["k_tokens"].shape[2]
+    kt, vt = x["k_tokens"][:, :, :T].contiguous().cuda(), x["v_tokens"][:, :, :T].contiguous().cuda()
+    nblk = -(-T // w.block_len)
+    qs = x["q_steps"][:nblk].cuda()
+
+    def trace(overlap):
+        loop = drivers.BlockLoop(s.layers, s.q_heads, s.kv_heads, s.head_dim, torch.bfloat16,
+                                 w.block_len, w.budget_m, s.n_sinks, s.q_per_chunk,
+                                 overlap_v=overlap)
+        recs = []
+        prev = {"n": w.budget_m - 5 if case == "loaded" else 0}
+
+        def on_step(b, lp, did):
+            n = prev["n"] + min(w.block_len, T - b * w.block_len)   # rows scored by this step
+            prev["n"] = lp.n
+            if did:   # both written on the caller's stream: no join needed
+                recs.append((b, lp.scores[:s.layers * s.kv_heads * n].clone(), lp.kept.clone()))
+
+        if case == "loaded":
+            loop.load_cache(kt, vt, w.budget_m - 5)
+            for b in range(1, nblk):
+                on_step(b, loop, loop.step(b, kt, vt, qs[b]))
+        else:
+            loop.run(kt, vt, qs, on_step=on_step)
+        ck, cv = loop.cache_view()
+        out = (recs, ck.clone(), cv.clone())
+        torch.cuda.synchronize()
+        return out
+
+    one, two = trace(False), trace(True)
+    assert len(one[0]) == len(two[0]) and len(one[0]) >= 2
+    for (b1, s1, k1), (b2, s2, k2) in zip(one[0], two[0]):
+        assert b1 == b2 and torch.equal(s1, s2) and torch.equal(k1, k2), b1
+    assert torch.equal(one[1].view(torch.int16), two[1].view(torch.int16))
+    assert torch.equal(one[2].view(torch.int16), two[2].view(torch.int16))
+
+
 @pytest.mark.parametrize("T", [1100, 900])
 def test_block_loop_ragged_and_uncompressed_streams(K, T):
     """Token streams cut short of the workload's: at T = 1100 the first
