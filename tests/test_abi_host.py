@@ -220,6 +220,38 @@ def seg(K, k_head=None, v_head=None, head_rows=0, head_row_stride=0, k_tail=None
                            tail_row_stride)
 
 
+def test_compact_planes_and_segments_reject_bad_arguments(K):
+    """kvs_compact / kvs_compact_seg with one tensor left out (NULL): the
+    pointers of the tensor that is gathered are still checked; leaving out both
+    is an error; the segments are checked as in kvs_compress_block_seg.  Every
+    call here fails before any launch."""
+    h = raw(K)
+    p = prob(K)                                       # N = 4300, kv_row_stride 0
+    ks = (ctypes.c_int64 * 2)(100, 200)
+    assert h.kvs_compact(ctypes.byref(p), FAKE, FAKE, FAKE, ks, None, None, 0, None) == 1
+    assert h.kvs_compact(ctypes.byref(p), None, FAKE, FAKE, ks, FAKE, None, 0, None) == 1
+    assert h.kvs_compact(ctypes.byref(p), None, FAKE, FAKE, ks, None, FAKE + 4, 0, None) == 5
+    assert h.kvs_compact(ctypes.byref(p), FAKE, None, FAKE, ks, FAKE + 4, None, 0, None) == 5
+    good = dict(k_head=FAKE, v_head=FAKE, head_rows=4096, head_row_stride=6144, k_tail=FAKE,
+                v_tail=FAKE, tail_row0=2048, tail_row_stride=16384)
+
+    def call(sg, ko=FAKE, vo=None, stride=0, prob_=p, kept=FAKE):
+        return h.kvs_compact_seg(ctypes.byref(prob_), ctypes.byref(sg) if sg is not None else None,
+                                 kept, ks, ko, vo, stride, None)
+
+    assert call(None) == 1
+    assert call(seg(K, **good), prob_=prob(K, kv_row_stride=4300)) == 2
+    assert call(seg(K, **dict(good, head_rows=4093))) == 2
+    assert call(seg(K, **dict(good, tail_row_stride=2048 + 203))) == 2
+    assert call(seg(K, **good), stride=-1) == 2
+    assert call(seg(K, **good), stride=150) == 4        # k_l = 200 > out_row_stride
+    assert call(seg(K, **good), ko=None, vo=None) == 1
+    assert call(seg(K, **good), kept=None) == 1
+    assert call(seg(K, **dict(good, k_tail=None))) == 1             # K gathered: its tail is read
+    assert call(seg(K, **dict(good, k_head=None, k_tail=None)), ko=None, vo=FAKE + 4) == 5
+    assert call(seg(K, **dict(good, v_head=FAKE + 8)), ko=None, vo=FAKE) == 5
+
+
 def test_compress_block_seg_rejects_bad_segments(K):
     h = raw(K)
     p = prob(K)   # N = 4300
