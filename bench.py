@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true",
                     help="time without per-launch events (for profiler runs)")
+    ap.add_argument("--overlap-v", action="store_true",
+                    help="block loop: gather V on a second stream beside the next step's scoring")
     return ap.parse_args()
 
 
@@ -78,7 +80,8 @@ def main():
     if w.kind == "block_loop":
         x = gen.block_loop_inputs(w, device=dev)
         loop = drivers.BlockLoop(s.layers, s.q_heads, s.kv_heads, s.head_dim, torch.bfloat16,
-                                 w.block_len, w.budget_m, s.n_sinks, s.q_per_chunk, device=dev)
+                                 w.block_len, w.budget_m, s.n_sinks, s.q_per_chunk, device=dev,
+                                 overlap_v=args.overlap_v)
         calls = []
         n = 0
         for b in range(w.n_blocks):
@@ -222,7 +225,9 @@ def main():
         "config": {"workload": w.name, "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "n_cache_per_call": n_step, "scoring_calls_per_step": len(calls),
                    "scored_tokens_per_step": tokens, "keep_per_layer": kl[0] if kl else None,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "v_gather": "second stream" if (w.kind == "block_loop" and args.overlap_v)
+                   else "same stream"},
         "roofline": roofline,
         "score_mfma_frac": round(all_flops / (score_ms * 1e-3) / 1e12 / peak, 4) if score_ms else None,
         "select_compact_GBps": round((sel_bytes + cmp_bytes) / (sc_ms * 1e-3) / 1e9, 1) if sc_ms else None,
