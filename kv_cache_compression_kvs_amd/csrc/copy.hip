@@ -129,25 +129,34 @@ __global__ __launch_bounds__(kThreads) void compact_ragged_kernel(RaggedArgs a) 
   constexpr int RPP = kThreads / LPR;
   __shared__ int32_t first_unit;
   const int64_t t0 = (int64_t)blockIdx.x * (RPP * kUnroll);
-  if (threadIdx.x == 0) {
-    int32_t lo = 0, hi = a.units - 1;  // last unit whose list starts at or before t0
-    while (lo < hi) {
-      const int32_t mid = (lo + hi + 1) >> 1;
-      if (a.offsets[mid] <= t0) lo = mid;
-      else hi = mid - 1;
-    }
-    first_unit = lo;
+  if (threadIdx.x < 64) {
+    // The last unit whose list starts at or before t0.  offsets is
+    // non-decreasing with offsets[0] = 0, so that is the count of units
+    // starting at or before t0, minus one: independent loads, one per lane
+    // and 64 units, instead of a binary search's chain of dependent ones.
+    int32_t c = 0;
+    for (int32_t j = threadIdx.x; j < a.units; j += 64) c += a.offsets[j] <= t0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+    if (threadIdx.x == 0) first_unit = c > 0 ? c - 1 : 0;
   }
   __syncthreads();
   const int piece = threadIdx.x % LPR;
   const int rsub = threadIdx.x / LPR;
   int64_t slab[kUnroll], idx[kUnroll];
   bool ok[kUnroll];
-  int32_t u = first_unit;
+  const int32_t u0 = first_unit;
+  // the workgroup's rows nearly always lie in u0 or the units right after it:
+  // u0's end is loaded once, and only rows past it walk on
+  const int64_t end0 = u0 + 1 < a.units ? a.offsets[u0 + 1] : INT64_MAX;
 #pragma unroll
   for (int k = 0; k < kUnroll; ++k) {
     const int64_t t = t0 + k * RPP + rsub;
-    while (u + 1 < a.units && a.offsets[u + 1] <= t) ++u;
+    int32_t u = u0;
+    if (t >= end0) {
+      ++u;
+      while (u + 1 < a.units && a.offsets[u + 1] <= t) ++u;
+    }
     const int64_t i = a.kept[min(t, a.total - 1)];
     ok[k] = t < a.total && i >= 0 && i < a.n_cache;  // rows outside the cache are skipped
     idx[k] = ok[k] ? i : 0;
