@@ -84,6 +84,7 @@ Every pin of these functions lives in tests/test_oracle_*.py.
 from __future__ import annotations
 
 import math
+from functools import partial
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -161,12 +162,20 @@ def chunk_scores(q_group: np.ndarray, keys: np.ndarray, r: int, n_sinks: int,
 
 
 def unit_scores(q_group: np.ndarray, keys: np.ndarray, n_sinks: int, chunk_size: int,
-                q_per_chunk: int, row_block: int = 64) -> np.ndarray:
-    """Scores of every position of one (layer, KV head): [N], sinks = 1."""
+                q_per_chunk: int, row_block: int = 64, chunk_map=map) -> np.ndarray:
+    """Scores of every position of one (layer, KV head): [N], sinks = 1.
+
+    The chunks are independent; ``chunk_map(f, chunk_indices)`` evaluates f on
+    each of them (the builtin map by default; a test may pass a parallel map,
+    which changes nothing in what is computed)."""
     n_cache = keys.shape[0]
+    bounds = chunk_bounds(n_cache, n_sinks, chunk_size)
+    parts = list(chunk_map(partial(chunk_scores, q_group, keys, n_sinks=n_sinks,
+                                   chunk_size=chunk_size, q_per_chunk=q_per_chunk,
+                                   row_block=row_block), range(len(bounds))))
     s = np.zeros(n_cache, np.float64)
-    for r, (a, b) in enumerate(chunk_bounds(n_cache, n_sinks, chunk_size)):
-        s[a:b] = chunk_scores(q_group, keys, r, n_sinks, chunk_size, q_per_chunk, row_block)
+    for (a, b), part in zip(bounds, parts):
+        s[a:b] = part
     s[:min(n_sinks, n_cache)] = 1.0
     return s
 
@@ -369,19 +378,6 @@ def token_scores(score: np.ndarray) -> np.ndarray:
     """p_i: the mean over layers and KV heads of score[l, g, i]  ([L, Hkv, N] -> [N])."""
     s = np.asarray(score, np.float64)
     return s.reshape(-1, s.shape[-1]).mean(axis=0)
-
-
-def token_sums_f32(score: np.ndarray) -> np.ndarray:
-    """The GPU's ranking key for p: the float32 sum over (l, g), layer-major, one
-    unit at a time.  Dividing by L * Hkv would not change the order, so the
-    sum is ranked directly; both sides must round the same way because the
-    ranking decides which positions are chosen."""
-    s = np.asarray(score, np.float32)
-    s = s.reshape(-1, s.shape[-1])
-    acc = np.zeros(s.shape[1], np.float32)
-    for u in range(s.shape[0]):
-        acc = np.add(acc, s[u], dtype=np.float32)
-    return acc
 
 
 def select_queries(p: np.ndarray, n_cache: int, n_sinks: int, chunk_size: int,

@@ -7,8 +7,17 @@ Tolerances:
   kept     exact, except positions whose oracle score lies within 2e-3 (relative)
            of the oracle's threshold tau, the (k - S)-th best non-sink score:
            there the float64 and fp32 orders may legitimately differ.
+  queries  (stage-1 selection from a score tensor) the float64 mean of the
+           oracle decides; the GPU ranks by a float32 sum over the L * Hkv
+           units, whose error is at most (U - 1) 2^-24 of the sum (recursive
+           summation of non-negative terms), so a position may differ from the
+           oracle's set only if its mean lies within 2 U 2^-24 of the chunk's
+           cut-off, relative.
 """
 from __future__ import annotations
+
+import multiprocessing
+import os
 
 import numpy as np
 import torch
@@ -86,3 +95,61 @@ def assert_valid_selection(scores_row: torch.Tensor, kept_row: torch.Tensor, k: 
             tie_in = idx[mask & (s == worst_in)].max()
             tie_out = idx[out & (s == best_out)].min()
             assert tie_in < tie_out, f"{what}: tie broken toward a higher position"
+
+
+def assert_queries_match_f64(got, score64, n_cache, n_sinks, chunk_size, rho, what=""):
+    """GPU per-chunk query positions vs the oracle's selection on the float64
+    mean over (layer, KV head) of score64 [L, Hkv, N].  Counts, order and range
+    are exact; membership may differ only inside the float32 rounding band of
+    the chunk's cut-off.  Returns the number of positions that differ."""
+    s = np.asarray(score64, np.float64)
+    U = int(np.prod(s.shape[:-1]))
+    mean = O.token_scores(s)
+    want = O.select_queries(mean, n_cache, n_sinks, chunk_size, rho)
+    bounds = O.chunk_bounds(n_cache, n_sinks, chunk_size)
+    assert len(got) == len(want) == len(bounds), f"{what}: chunk count"
+    ndiff = 0
+    for r, ((a, b), x, y) in enumerate(zip(bounds, got, want)):
+        x = np.asarray(x, np.int64)
+        assert x.shape == y.shape, f"{what} chunk {r}: {x.shape[0]} positions, want {y.shape[0]}"
+        assert np.all(np.diff(x) > 0), f"{what} chunk {r}: not ascending"
+        assert x.size == 0 or (x[0] >= a and x[-1] < b), f"{what} chunk {r}: outside the chunk"
+        diff = set(x.tolist()) ^ set(y.tolist())
+        if not diff:
+            continue
+        cut = float(np.sort(mean[a:b])[::-1][len(y) - 1])
+        band = 2.05 * U * 2.0 ** -24 * abs(cut)
+        for i in diff:
+            assert abs(mean[i] - cut) <= band, f"{what} chunk {r}: position {i} mean {mean[i]!r} cut {cut!r}"
+        ndiff += len(diff)
+    return ndiff
+
+
+_TASK = None
+
+
+def _run_task(i):
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        return _TASK(i)
+
+
+def fork_map(f, items, procs: int = 8):
+    """list(map(f, items)) over a pool of forked worker processes.
+
+    Test plumbing for the oracle's independent pieces (for example the chunks
+    of one unit): f is handed to the workers through the fork, so its large
+    arguments are never pickled.  The workers run numpy only and never touch
+    the GPU; they leave through os._exit, so no exit handler of the parent's
+    GPU runtime runs in them."""
+    global _TASK
+    items = list(items)
+    procs = max(1, min(procs, len(items), os.cpu_count() or 1))
+    if procs == 1:
+        return [f(i) for i in items]
+    _TASK = f
+    try:
+        with multiprocessing.get_context("fork").Pool(procs) as pool:
+            return pool.map(_run_task, items)
+    finally:
+        _TASK = None

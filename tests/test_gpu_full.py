@@ -18,7 +18,8 @@ import torch
 from oracle import oracle as O
 from workloads import FULL, gen
 
-from gpu_util import assert_kept_match, assert_scores_close, f64
+from gpu_util import (assert_kept_match, assert_queries_match_f64, assert_scores_close, f64,
+                      fork_map)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -114,12 +115,13 @@ def test_kv2_full(K, name):
     R = s.n_chunks
     sampled_chunk_scores(w, x["q"], x["k"], [(0, 0, 0), (s.layers - 1, s.kv_heads - 1, R - 1),
                                              (s.layers // 2, 3, R // 2)], scores, name)
-    if name == "kv2_32k":   # one whole unit through the oracle's selection
-        l, g = 5, 2
-        o = O.unit_scores(f64(x["q"][l, g * s.group:(g + 1) * s.group]), f64(x["k"][l, g]),
-                          s.n_sinks, s.chunk_size, s.q_per_chunk)
-        assert_scores_close(f64(scores[l, g]), o, f"{name} unit ({l},{g})")
-        assert_kept_match(layers[l][g].cpu().numpy(), o, keep, s.n_sinks, f"{name} unit ({l},{g})")
+    # one whole unit, every chunk, through the oracle's scores and selection
+    l, g = (5, 2) if name == "kv2_32k" else (s.layers - 2, 6)
+    o = O.unit_scores(f64(x["q"][l, g * s.group:(g + 1) * s.group]), f64(x["k"][l, g]),
+                      s.n_sinks, s.chunk_size, s.q_per_chunk, chunk_map=fork_map)
+    worst = assert_scores_close(f64(scores[l, g]), o, f"{name} unit ({l},{g})")
+    nd = assert_kept_match(layers[l][g].cpu().numpy(), o, keep, s.n_sinks, f"{name} unit ({l},{g})")
+    print(f"{name} unit ({l},{g}): max rel err {worst:.2e}, {nd} kept positions in the tie band")
     check_selection_all(scores, layers, s.n_sinks, name)
     check_compaction(x["k"], x["v"], layers, ko, vo, name)
     # refinement: these stage-2 scores choose the next pass's queries
@@ -129,10 +131,14 @@ def test_kv2_full(K, name):
     pos = torch.full((int(counts.sum()),), -1, dtype=torch.int32, device="cuda")
     K.kvs_query_select(p, scores.reshape(-1), 0.1, pos)
     torch.cuda.synchronize()
-    sc = scores.cpu().numpy()
-    want = np.concatenate(O.select_queries(O.token_sums_f32(sc), s.n_cache, s.n_sinks,
-                                           s.chunk_size, 0.1))
-    assert np.array_equal(pos.cpu().numpy().astype(np.int64), want), f"{name}: query selection"
+    sc = scores.cpu().numpy().astype(np.float64)
+    got, off = [], 0
+    for c in counts:
+        got.append(pos[off:off + int(c)].cpu().numpy().astype(np.int64))
+        off += int(c)
+    nd = assert_queries_match_f64(got, sc, s.n_cache, s.n_sinks, s.chunk_size, 0.1,
+                                  f"{name}: query selection")
+    print(f"{name}: query selection, {nd} positions inside the float32 rounding band")
     if name == "kv2_131k":  # planted needles: a sanity signal, most should survive at 2%
         needles = gen.needle_positions(s.n_cache, s.n_sinks).cuda()
         kept0 = layers[0][0].long()

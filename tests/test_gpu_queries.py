@@ -1,16 +1,19 @@
 """GPU stage-1 query selection against the oracle.
 
-The GPU ranks positions by the float32 layer-major sum of the per-unit scores,
-the same key the oracle's token_sums_f32 gives, so the positions must match
-exactly.  Against the float64 mean (the plain reading of the pages) the sets
-may differ only at positions whose mean lies within the float32 rounding of
-the sum (L * Hkv * 2^-24 relative) of the chunk's cut-off."""
+The oracle ranks positions by the float64 mean of the per-unit scores (the
+token score of the pages).  The GPU ranks by a float32 sum over the units,
+which orders like the mean up to its rounding, so the per-chunk lists must
+have the oracle's counts and order, and may hold other positions only where
+the mean lies within the float32 rounding of the sum (about L * Hkv * 2^-24,
+relative) of the chunk's cut-off."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import oracle as O
 from workloads import gen
+
+from gpu_util import assert_queries_match_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -35,19 +38,6 @@ def run_query_select(K, scores, L, Hkv, N, S, m, rho):
     return got, counts
 
 
-def check_against_f64(got, s64, N, S, m, rho, U):
-    mean = O.token_scores(s64)
-    want = O.select_queries(mean, N, S, m, rho)
-    for (a, b), x, y in zip(O.chunk_bounds(N, S, m), got, want):
-        diff = set(x.tolist()) ^ set(y.tolist())
-        if not diff:
-            continue
-        cut = np.sort(mean[a:b])[::-1][len(y) - 1]
-        band = U * 2.0 ** -24 * max(abs(cut), np.abs(mean[a:b]).max()) * 2
-        for i in diff:
-            assert abs(mean[i] - cut) <= band, (i, mean[i], cut)
-
-
 CASES = [
     # (L, Hkv, N, S, m, rho, kind)
     (2, 2, 300, 4, 100, 0.1, "uniform"),
@@ -67,11 +57,8 @@ def test_query_select_matches_oracle(K, case):
     scores = gen.score_tensor(L * Hkv, N, S, kind, seed=N + L).reshape(L, Hkv, N)
     got, counts = run_query_select(K, scores, L, Hkv, N, S, m, rho)
     assert counts.tolist() == O.query_counts(N, S, m, rho)
-    want = O.select_queries(O.token_sums_f32(scores.numpy()), N, S, m, rho)
-    assert len(got) == len(want)
-    for r, (x, y) in enumerate(zip(got, want)):
-        assert np.array_equal(x, y), f"chunk {r}"
-    check_against_f64(got, scores.double().numpy(), N, S, m, rho, L * Hkv)
+    ndiff = assert_queries_match_f64(got, scores.double().numpy(), N, S, m, rho, str(case))
+    print(f"{case}: {ndiff} positions inside the rounding band")
 
 
 def test_refinement_on_stage_two_scores(K):
@@ -88,5 +75,5 @@ def test_refinement_on_stage_two_scores(K):
     torch.cuda.synchronize()
     sc = scores.view(s.layers, s.kv_heads, s.n_cache).cpu()
     got, _ = run_query_select(K, sc, s.layers, s.kv_heads, s.n_cache, s.n_sinks, s.chunk_size, 0.1)
-    want = O.select_queries(O.token_sums_f32(sc.numpy()), s.n_cache, s.n_sinks, s.chunk_size, 0.1)
-    assert all(np.array_equal(a, b) for a, b in zip(got, want))
+    assert_queries_match_f64(got, sc.double().numpy(), s.n_cache, s.n_sinks, s.chunk_size, 0.1,
+                             "refinement")

@@ -41,28 +41,6 @@ def test_token_scores_closed_form():
     assert np.array_equal(O.token_scores(s), want)
 
 
-def test_token_sums_f32_rounding_and_order():
-    # sequential float32 sums, layer-major: 2^24 + 1 rounds back to 2^24 (ties
-    # to even) twice, so the sum stays 2^24 though the exact sum is 2^24 + 2
-    s = np.array([[[2.0 ** 24]], [[1.0]], [[1.0]]], np.float32)   # [L=3, H=1, N=1]
-    assert O.token_sums_f32(s)[0] == np.float32(2.0 ** 24)
-    # in the other order the two ones are added first and survive
-    s2 = np.array([[[1.0]], [[1.0]], [[2.0 ** 24]]], np.float32)
-    assert O.token_sums_f32(s2)[0] == np.float32(2.0 ** 24 + 2)
-    # small integers are exact: the sum is L * H times the mean
-    rng = np.random.default_rng(3)
-    s3 = rng.integers(0, 50, size=(4, 3, 40)).astype(np.float32)
-    assert np.array_equal(O.token_sums_f32(s3).astype(np.float64), 12 * O.token_scores(s3))
-
-
-def test_token_sums_f32_within_rounding_of_the_mean():
-    rng = np.random.default_rng(4)
-    s = rng.random((28, 8, 500)).astype(np.float32)
-    U = 28 * 8
-    err = np.abs(O.token_sums_f32(s).astype(np.float64) / U - O.token_scores(s))
-    assert err.max() <= U * 2.0 ** -24 * 1.0
-
-
 def dominates(p, i, j):
     return p[i] > p[j] or (p[i] == p[j] and i < j)
 
