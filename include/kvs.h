@@ -147,7 +147,8 @@ int kvs_score(const kvs_problem* p, const void* q, const void* k, float* scores,
  * ascending.  k_per_layer: HOST array [L] with S <= k_l <= N.
  * kept: device int32, packed layer after layer and head after head: the list
  * of (l, g) starts at Hkv * sum_{l'<l} k_l' + g * k_l and has k_l entries.
- * Scores compare as floats (-0 equals +0); NaN orders above +inf.
+ * Scores compare as floats (-0 equals +0); every NaN, of either sign and any
+ * payload, orders above +inf, and NaNs tie with each other (lower position first).
  * ws: device workspace of kvs_workspace_bytes(p) bytes, 256-byte aligned; it
  * is used (and then required, else KVS_E_NULL / KVS_E_WORKSPACE /
  * KVS_E_ALIGN) only when N - S exceeds 131072 candidates per (l, g).

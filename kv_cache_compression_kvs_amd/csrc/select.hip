@@ -40,8 +40,12 @@ constexpr int kBatch = 8;                 // candidates per thread per histogram
 constexpr int64_t kLdsKeys = 32 * 1024;   // candidates cached in LDS (128 KiB)
 static_assert(kLdsKeys == kSelSingleMax, "longer units go to the multi-workgroup select");
 
+// Order-preserving 32-bit key of a score: -0 reads as +0, and every NaN
+// (either sign, any payload) takes the one key above that of +inf, so NaNs
+// tie with each other and the lower position wins among them.
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0xFFFFFFFFu;
   if (b == 0x80000000u) b = 0u;
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }

@@ -162,16 +162,29 @@ def test_select_matches_oracle_exactly(K, case):
     assert np.array_equal(got[:total], want)
 
 
+# NaN bit patterns of both signs and several payloads: quiet and signalling,
+# the canonical positive one and the negative one an x86 host produces
+NAN_BITS = [0x7FC00000, -0x00400000, 0x7F800001, -0x00000001, 0x7FC12345, -0x007FFFFF]
+
+
 @pytest.mark.parametrize("N", [6144, 40000, 140000])
-def test_select_nan_orders_above_inf(K, N):
-    """The ABI orders NaN above +inf; every select path (LDS-resident, one
-    workgroup streaming, multi-workgroup) agrees.  The oracle sees the NaNs as
-    2.0, above every other score here, which gives the same order."""
-    S, ks = 4, [1500]
+@pytest.mark.parametrize("keep", [1500, 24])
+def test_select_nan_orders_above_inf(K, N, keep):
+    """The ABI orders every NaN (either sign, any payload) above +inf and ties
+    NaNs with each other; every select path (LDS-resident, one workgroup
+    streaming, multi-workgroup) agrees.  The oracle sees the NaNs as 2.0, above
+    every other score here, which gives the same order.  With keep = 24 there
+    are more NaNs than non-sink slots, so the tie order among NaNs decides."""
+    S, ks = 4, [keep]
     scores = gen.score_tensor(2, N, S, "uniform", seed=N + 11)
     g = torch.Generator().manual_seed(N)
     nan_pos = torch.randint(S, N, (2, 40), generator=g)
-    scores.scatter_(1, nan_pos, float("nan"))
+    bits = torch.tensor(NAN_BITS, dtype=torch.int32)
+    pick = torch.randint(0, len(NAN_BITS), (2, 40), generator=g)
+    scores.view(torch.int32).scatter_(1, nan_pos, bits[pick])
+    assert int(torch.isnan(scores).sum()) == int(torch.unique(nan_pos[0]).numel()
+                                                 + torch.unique(nan_pos[1]).numel())
+    assert bool((scores.view(torch.int32) < 0).logical_and(torch.isnan(scores)).any())
     p = K.make_problem(1, 2, 2, 128, N, S, N - S, 1, torch.bfloat16)
     kept = torch.full((2 * ks[0],), -7, dtype=torch.int32, device="cuda")
     K.kvs_select(p, scores.cuda(), ks, kept)
