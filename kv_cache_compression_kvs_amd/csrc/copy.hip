@@ -108,9 +108,10 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const uint8_t* src, in
 
 // Ragged compaction (global eviction): output row t belongs to the unit u
 // with offsets[u] <= t < offsets[u + 1] and is row kept[t] of that unit's
-// slab.  The grid covers the rows; thread 0 finds the workgroup's first unit
-// by binary search and each row walks forward from it (a workgroup's rows
-// rarely cross more than one unit boundary).
+// slab.  The grid covers the rows; the first wave finds the workgroup's first
+// unit by counting the units that start at or before its first row (one load
+// per lane per 64 units, all independent), and each row walks forward from it
+// (a workgroup's rows rarely cross more than one unit boundary).
 struct RaggedArgs {
   const uint8_t* kh;
   const uint8_t* vh;

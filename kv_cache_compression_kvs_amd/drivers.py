@@ -76,10 +76,14 @@ class BlockLoop:
             torch.cuda.current_stream().wait_event(self._v_done)
             self._v_done = None
 
-    def _compress(self, compress_k: Callable, gather_v: Callable, nxt: int) -> None:
+    def _compress(self, compress_k: Callable, gather_v: Callable, nxt: int,
+                  v_reads: Sequence[torch.Tensor] = ()) -> None:
         """One compression: compress_k(kept, v_out) scores, selects and gathers
         K (and V when v_out is given) on the caller's stream and returns the
-        per-layer budgets; gather_v(kept, budgets) gathers V."""
+        per-layer budgets; gather_v(kept, budgets) gathers V.  v_reads are the
+        caller's tensors the V gather reads: with overlap_v they are marked as
+        used on the second stream, so the caching allocator keeps their memory
+        until that gather has finished even if the caller frees them first."""
         i = self._ki
         self._ki ^= 1
         kept = self._kept[i]
@@ -94,6 +98,8 @@ class BlockLoop:
             ready.record(main)
             with torch.cuda.stream(self.side):
                 self.side.wait_event(ready)
+                for t in v_reads:
+                    t.record_stream(self.side)
                 gather_v(kept, kl)
                 done = torch.cuda.Event()
                 done.record(self.side)
@@ -133,7 +139,12 @@ class BlockLoop:
         reads the kept cache and the block where they lie (two segments) and
         gathers the kept rows of both into the other buffer.  Before the first
         compression the cache is rows [0, n) of the token buffer itself, so
-        that compression reads one strided segment and nothing is copied."""
+        that compression reads one strided segment and nothing is copied.
+
+        With overlap_v the V gather of this step may still be reading v_tokens
+        on the second stream when step() returns.  Freeing v_tokens is safe
+        (its memory is not reused before the gather ends), but writing into it
+        in place is not: call join() first."""
         T = k_tokens.shape[2]
         r0 = b * self.B
         nb = min(self.B, T - r0)
@@ -155,7 +166,7 @@ class BlockLoop:
                     kept, self.k[nxt], v_out, out_row_stride=self.cap, ws=self.ws),
                 lambda kept, kl: api.kvs_compact(p, None, v_tokens, kept, kl, None, self.v[nxt],
                                                  out_row_stride=self.cap),
-                nxt)
+                nxt, (v_tokens,))
             self._tok = None
             self.cur = nxt
             self.n = self.M
@@ -171,7 +182,7 @@ class BlockLoop:
                 lambda kept, kl: api.kvs_compact_seg(
                     p, None, self.v[cur], n, self.cap, None, v_tokens, r0, T, kept, kl, None,
                     self.v[nxt], out_row_stride=self.cap),
-                nxt)
+                nxt, (v_tokens,))
             self.cur = nxt
             self.n = self.M
             return True
