@@ -55,8 +55,12 @@ typedef enum kvs_status {
   KVS_E_BUDGET = 4,    /* a budget outside [n_sinks, n_cache], or bad sensitivities */
   KVS_E_ALIGN = 5,     /* a device pointer is not 16-byte aligned */
   KVS_E_WORKSPACE = 6, /* workspace smaller than kvs_workspace_bytes() */
-  KVS_E_HIP = 7        /* a HIP launch or runtime call failed */
+  KVS_E_HIP = 7,       /* a HIP launch or runtime call failed */
+  KVS_E_SCRATCH = 8    /* needs more than KVS_NOALLOC_SCRATCH_BYTES of scratch */
 } kvs_status;
+
+/* Scratch that kvs_compress_block_noalloc holds per GPU (64 MiB). */
+#define KVS_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
 
 typedef enum kvs_dtype {
   KVS_F32 = 0,  /* float32 queries and keys (scored with fp32 vector arithmetic) */
@@ -189,6 +193,28 @@ int kvs_compress_block(const kvs_problem* p, const void* q, const void* k, const
                        float* scores, int32_t* kept, void* k_out, void* v_out,
                        int64_t out_row_stride, int64_t* k_per_layer_out,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kvs_compress_block for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as kvs_compress_block, minus
+ * the workspace: the scratch the kernels need comes from a device array of
+ * KVS_NOALLOC_SCRATCH_BYTES built into the library, one per GPU (the GPU of
+ * `stream`, or the current device for a NULL stream), which that GPU holds
+ * from the first call on it until the process ends.  The call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine).
+ * Returns KVS_E_SCRATCH, before touching the device, when the problem needs
+ * more scratch than that (kvs_workspace_bytes(p) covers it; the 131,072-token
+ * KV² shape of 36 layers x 32 query heads needs about 60 MB).  Every call on
+ * one GPU shares its array and finds the previous call's contents there; the
+ * kernels write everything they read from it first.  Calls that overlap on
+ * one GPU (two streams, two threads) race on the array: serialise them.
+ */
+int kvs_compress_block_noalloc(const kvs_problem* p, const void* q, const void* k,
+                               const void* v, int64_t total_budget, const double* sens,
+                               double alpha, float* scores, int32_t* kept, void* k_out,
+                               void* v_out, int64_t out_row_stride, int64_t* k_per_layer_out,
+                               void* stream);
 
 /*
  * The cache of one compression split in two buffers, as in the block-prefill

@@ -6,7 +6,8 @@ include/kvs.h); this package only marshals arguments and sequences calls.
 from ._lib import (KVS_BF16, KVS_F32, KvsKvSegments, KvsLibraryMissing,  # noqa: F401
                    KvsProblem, LIB_PATH)
 from .api import (KvsError, kvs_append_rows, kvs_check_problem, kvs_compact,  # noqa: F401
-                  kvs_compact_ragged, kvs_compact_seg, kvs_compress_block, kvs_compress_block_seg,
+                  kvs_compact_ragged, kvs_compact_seg, kvs_compress_block,
+                  kvs_compress_block_noalloc, kvs_compress_block_seg,
                   kvs_compress_global, kvs_decode_ragged, kvs_decode_workspace_bytes,
                   kvs_key_similarity, kvs_kmeans, kvs_kmeans_workspace_bytes,
                   kvs_layer_budgets, kvs_match_episodes, kvs_medoids, kvs_medoids_workspace_bytes, kvs_select_global,

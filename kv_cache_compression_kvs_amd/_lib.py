@@ -22,7 +22,8 @@ P_F64 = ctypes.POINTER(ctypes.c_double)
 
 KVS_F32, KVS_BF16 = 0, 1
 STATUS_NAMES = {0: "KVS_OK", 1: "KVS_E_NULL", 2: "KVS_E_SHAPE", 3: "KVS_E_DTYPE",
-                4: "KVS_E_BUDGET", 5: "KVS_E_ALIGN", 6: "KVS_E_WORKSPACE", 7: "KVS_E_HIP"}
+                4: "KVS_E_BUDGET", 5: "KVS_E_ALIGN", 6: "KVS_E_WORKSPACE", 7: "KVS_E_HIP",
+                8: "KVS_E_SCRATCH"}
 
 
 class KvsProblem(ctypes.Structure):
@@ -68,6 +69,10 @@ SIGNATURES = {
     "kvs_compress_block": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p, c_void_p, c_void_p,
                                      c_int64, P_F64, c_double, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_int64, P_I64, c_void_p, c_size_t, c_void_p]),
+    "kvs_compress_block_noalloc": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p, c_void_p,
+                                             c_void_p, c_int64, P_F64, c_double, c_void_p,
+                                             c_void_p, c_void_p, c_void_p, c_int64, P_I64,
+                                             c_void_p]),
     "kvs_compress_block_seg": (c_int32, [ctypes.POINTER(KvsProblem), c_void_p,
                                          ctypes.POINTER(KvsKvSegments), c_int64, P_F64, c_double,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_int64, P_I64,

@@ -168,6 +168,22 @@ def kvs_compress_block(p: KvsProblem, q: Tensorish, k: Tensorish, v: Tensorish, 
     return np.array(kl[:], dtype=np.int64)
 
 
+def kvs_compress_block_noalloc(p: KvsProblem, q: Tensorish, k: Tensorish, v: Tensorish,
+                               total_budget: int, sens: Optional[Sequence[float]], alpha: float,
+                               scores: Tensorish, kept: Tensorish, k_out: Tensorish,
+                               v_out: Tensorish, out_row_stride: int = 0,
+                               stream=None) -> np.ndarray:
+    """kvs_compress_block with the library's own per-GPU scratch instead of a
+    workspace (for callers that cannot allocate); returns the per-layer budgets."""
+    kl = (ctypes.c_int64 * p.layers)()
+    _check(_lib.lib().kvs_compress_block_noalloc(
+        ctypes.byref(p), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), total_budget, _f64(sens),
+        float(alpha), _dev(scores, "scores"), _dev(kept, "kept"), _dev(k_out, "k_out"),
+        _dev(v_out, "v_out"), out_row_stride, kl, _stream(stream)),
+        "kvs_compress_block_noalloc")
+    return np.array(kl[:], dtype=np.int64)
+
+
 def kvs_compress_block_seg(p: KvsProblem, q: Tensorish, k_head: Tensorish, v_head: Tensorish,
                            head_rows: int, head_row_stride: int, k_tail: Tensorish,
                            v_tail: Tensorish, tail_row0: int, tail_row_stride: int,

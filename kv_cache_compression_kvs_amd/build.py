@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["score_bf16.hip", "score_f32.hip", "select.hip", "copy.hip", "decode.hip",
-               "calib.hip", "cluster.hip", "trace.hip"]
+               "calib.hip", "cluster.hip", "trace.hip", "scratch.hip"]
 HOST_SOURCES = ["kvs_api.cpp"]
 
 # Packed fp32 instructions (v_pk_fma_f32 and friends) are kept out of every

@@ -332,6 +332,9 @@ const char* kvs_status_string(int status) {
     case KVS_E_ALIGN: return "a device pointer is not suitably aligned";
     case KVS_E_WORKSPACE: return "workspace is smaller than kvs_workspace_bytes()";
     case KVS_E_HIP: return "a HIP launch or runtime call failed";
+    case KVS_E_SCRATCH:
+      return "the problem needs more scratch than the allocation-free entry point holds "
+             "(KVS_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -428,6 +431,24 @@ int kvs_compress_block(const kvs_problem* p, const void* q, const void* k, const
   if (st) return st;
   return compress(*p, q, single_src(*p, k, v), total_budget, sens, alpha, scores, kept, k_out,
                   v_out, out_row_stride, k_per_layer_out, ws, ws_bytes, stream);
+}
+
+int kvs_compress_block_noalloc(const kvs_problem* p, const void* q, const void* k,
+                               const void* v, int64_t total_budget, const double* sens,
+                               double alpha, float* scores, int32_t* kept, void* k_out,
+                               void* v_out, int64_t out_row_stride, int64_t* k_per_layer_out,
+                               void* stream) {
+  int st = check(p);
+  if (st) return st;
+  // scratch the kernels of this call use: the scoring plan's, and the
+  // multi-workgroup select's when the cache takes that path
+  size_t need = plan_score(*p).ws_bytes;
+  if (select_uses_multi(*p)) need = std::max(need, select_ws_layout(*p).bytes);
+  if (need > (size_t)KVS_NOALLOC_SCRATCH_BYTES) return KVS_E_SCRATCH;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(stream, &ws))) return st;
+  return compress(*p, q, single_src(*p, k, v), total_budget, sens, alpha, scores, kept, k_out,
+                  v_out, out_row_stride, k_per_layer_out, ws, KVS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int kvs_compress_block_seg(const kvs_problem* p, const void* q, const kvs_kv_segments* seg,

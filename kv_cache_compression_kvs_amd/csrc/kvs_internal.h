@@ -35,6 +35,10 @@ struct LayerTable {
 
 ScorePlan plan_score(const kvs_problem& p);
 
+// Device address of the allocation-free scratch array on the GPU of `stream`
+// (the current device when stream is NULL); KVS_OK or KVS_E_HIP.
+int noalloc_scratch(void* stream, void** addr);
+
 // Where the cached rows live.  Row i of slab s = l * Hkv + g is row
 // s * head_stride + i of the head buffers for i < split, and row
 // s * tail_stride + tail_row0 + (i - split) of the tail buffers otherwise.

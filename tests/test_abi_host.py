@@ -203,6 +203,27 @@ def test_compress_block_rejects_infeasible_budget(K):
     assert st == 6
 
 
+def test_noalloc_rejects_before_touching_the_device(K):
+    """The allocation-free entry point checks the problem and its scratch need
+    before it looks up the device: an invalid problem gives KVS_E_SHAPE and a
+    problem beyond KVS_NOALLOC_SCRATCH_BYTES gives KVS_E_SCRATCH (both without
+    a GPU), and the budgets output is left as it was."""
+    h = raw(K)
+    kl = (ctypes.c_int64 * 128)(*([-7] * 128))
+    bad = prob(K, head_dim=96)
+    st = h.kvs_compress_block_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, 100, None, 0.0, FAKE,
+                                      FAKE, FAKE, FAKE, 0, kl, None)
+    assert st == 2
+    # 128 layers x 32 query heads x 20 chunks x 410 rows of fp32 row statistics
+    big = prob(K, layers=128, q_heads=32, kv_heads=8, n_cache=4 + 20 * 4096, chunk_size=4096,
+               q_per_chunk=410)
+    assert K.kvs_workspace_bytes(big) > 64 * 1024 * 1024
+    st = h.kvs_compress_block_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, 2621 * 128, None, 0.0,
+                                      FAKE, FAKE, FAKE, FAKE, 0, kl, None)
+    assert st == 8 and list(kl) == [-7] * 128
+    assert b"KVS_NOALLOC_SCRATCH_BYTES" in h.kvs_status_string(8)
+
+
 def test_append_rejects_bad_ranges(K):
     h = raw(K)
     assert h.kvs_append_rows(4, 128, 1, FAKE, 100, 90, 20, FAKE, 200, 0, None) == 2
