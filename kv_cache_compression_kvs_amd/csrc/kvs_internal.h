@@ -93,6 +93,11 @@ int launch_append(int32_t slabs, int64_t row_bytes, const void* src, int64_t src
 // workspace it carves (per-unit mode for long caches, and the global mode).
 constexpr int64_t kSelSpan = 4096;
 constexpr int64_t kSelSingleMax = 32 * 1024;
+// Per-unit selection of more candidates than this takes the one-workgroup
+// streaming select (a sampled bracket and one read of the scores) instead of
+// the LDS-resident radix select: measured on the 32K-token KV² shape (32,764
+// candidates per unit), 35 against 69 microseconds per call.
+constexpr int64_t kSelLongMin = 8 * 1024;
 // Per-unit selection streams up to this many candidates per unit in one
 // workgroup (bitmaps of them in LDS) and needs no workspace up to it.
 constexpr int64_t kSelLongMax = 128 * 1024;

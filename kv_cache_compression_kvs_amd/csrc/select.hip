@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void query_select_kernel(QueryArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// Per-unit select for long caches: kSelSingleMax < candidates <= kLongMax.
+// Per-unit select for long caches: kSelLongMin < candidates <= kLongMax.
 //
 // One 512-thread workgroup per (layer, KV head).  The cost of a pass over the
 // unit's keys is the work per key, which one CU does alone, so the common
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kLT, 4) void select_long_kernel(SelArgs a) {
   const int64_t S = a.S < N ? a.S : N;
   const float* srow = a.scores + unit * N + S;
   int32_t* out = a.kept + a.t.off[l] + g * kl;
-  const int64_t nc = N - S;  // in (kSelSingleMax, kLongMax]
+  const int64_t nc = N - S;  // in (kSelLongMin, kLongMax]
   const int64_t need = kl - S;
 
   for (int64_t i = tid; i < S; i += kLT) out[i] = (int32_t)i;
@@ -1301,7 +1301,7 @@ int launch_select(const kvs_problem& p, const float* scores, const LayerTable& t
   a.Hkv = p.kv_heads;
   a.t = t;
   TraceScope ts("select", st);
-  if (nc > kLdsKeys)
+  if (nc > kSelLongMin)
     hipLaunchKernelGGL(select_long_kernel, dim3((unsigned)units), dim3(kLT), 0, st, a);
   else
     hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)units), dim3(kThreads), 0, st, a);

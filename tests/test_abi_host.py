@@ -161,7 +161,7 @@ def test_score_rejects_bad_arguments(K):
     assert h.kvs_score(None, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
     assert h.kvs_score(ctypes.byref(p), None, FAKE, FAKE, FAKE, ws, None) == 1
     assert h.kvs_score(ctypes.byref(p), FAKE, None, FAKE, FAKE, ws, None) == 1
-    assert h.kvs_score(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ws - 1, None) == 6
+    assert h.kvs_score(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1, None) == 6
     assert h.kvs_score(ctypes.byref(p), FAKE + 2, FAKE, FAKE, FAKE, ws, None) == 5
     assert h.kvs_score(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE + 16, ws, None) == 5
     bad = prob(K, head_dim=80)

@@ -127,10 +127,16 @@ SEL = [
     (1, 2, 5000, 4, "sparse", [4, 300]),
     (2, 1, 6144, 4, "tiny", [4096]),
     (2, 1, 6144, 4, "coarse", [4096]),
-    (1, 1, 32768, 4, "uniform", [1638]),        # LDS-resident path, largest size
-    (1, 1, 40000, 4, "coarse", [2000]),          # global-memory path
-    (1, 1, 32772, 4, "uniform", [1000]),         # exactly fills the LDS cache
-    (1, 1, 32773, 4, "uniform", [1000]),         # one candidate too many: global path
+    (1, 1, 8196, 4, "uniform", [400]),          # 8,192 candidates: the LDS-resident path's largest
+    (1, 1, 8197, 4, "uniform", [400]),          # one more: the streaming select
+    (2, 1, 9000, 4, "coarse", [4500]),          # streaming select, heavy ties, half kept
+    (2, 1, 12000, 4, "tiny", [300]),            # streaming select, denormals and zeros
+    (2, 1, 20000, 4, "equal", [1000]),          # streaming select, every key equal
+    (2, 1, 30000, 0, "narrow", [9000]),         # streaming select, one top bin, no sinks
+    (1, 1, 32768, 4, "uniform", [1638]),        # the KV² 32K shape's candidate count
+    (1, 1, 40000, 4, "coarse", [2000]),
+    (1, 1, 32772, 4, "uniform", [1000]),
+    (1, 1, 32773, 4, "uniform", [1000]),
     (2, 1, 100003, 4, "sparse", [5000]),         # global path, ragged batches
     (1, 1, 131072, 4, "uniform", [2621]),
     (1, 1, 131072, 4, "equal", [2621]),          # every key equal: tau fixed by the histograms
