@@ -158,13 +158,14 @@ constexpr int64_t kMaxEmbedDim = 2048;
 constexpr int64_t kMaxMedoidPoints = 32 * 65535;  // 32-point tiles, grid y below 2^16
 
 // Pass-1 tiling constants shared by the planner and the kernels.
-constexpr int kP1Rows = 256;      // query rows per pass-1 workgroup (4 waves x 64)
+constexpr int kP1Waves = 4;       // pass-1 waves per workgroup, 64 query rows each
+constexpr int kP1Rows = kP1Waves * 64;  // query rows per pass-1 workgroup
 constexpr int kP1Keys = 128;      // keys per pass-1 LDS tile
 constexpr int kP1Ring = 2;        // pass-1 LDS tiles in flight
 constexpr int kP2Waves = 4;       // pass-2 waves per workgroup, 64 keys each
 constexpr int kP2Keys = kP2Waves * 64;  // keys per pass-2 workgroup
 constexpr int kP2Ring = 3;        // pass-2 LDS query tiles in flight
 constexpr int kMaxSplits = 64;
-constexpr int kP1Slots = 512;     // resident pass-1 workgroups: 2 per CU x 256 CUs
+constexpr int kP1Slots = 2048 / kP1Waves;  // resident pass-1 workgroups: 2 waves per SIMD, 1,024 SIMDs
 
 }  // namespace kvs

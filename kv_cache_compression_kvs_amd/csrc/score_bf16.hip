@@ -18,7 +18,7 @@
 //           loop is MFMA plus one running max per element, and a single exp2
 //           per position at the end (max of exp = exp of max).
 //
-// Pass 1 workgroup: 4 waves x 64 query rows (two 32-column MFMA blocks per
+// Pass 1 workgroup: W waves x 64 query rows (two 32-column MFMA blocks per
 // wave, Q fragments resident in VGPRs); keys stream through a ring of LDS
 // tiles filled by direct global->LDS loads.  Pass 2 workgroup: 64 keys per
 // wave resident in VGPRs; the chunk's query rows (all heads of the group)
@@ -49,15 +49,18 @@ struct P1Args {
   float c1, inv_c1;
 };
 
-template <int D, int TK, int NBUF>
-__global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
+// Two waves per SIMD whatever W is (8 / W workgroups per CU): about 200
+// VGPRs per wave.
+template <int D, int TK, int NBUF, int W>
+__global__ __launch_bounds__(W * 64, 8 / W) void pass1_bf16(P1Args a) {
+  constexpr int NT = W * 64;                       // threads per workgroup
   constexpr int KS = D / 16;                       // MFMA steps along d
   constexpr int ROWB = D * 2;                      // bytes per key row
   constexpr int CPR = ROWB / 16;                   // 16-byte chunks per row
   constexpr int NB = TK / 32;                      // 32-key blocks per tile
   constexpr int TILEB = TK * ROWB;                 // bytes per key tile
-  constexpr int LPT = TILEB / (kThreads * 16);     // DMA instructions per wave per tile
-  static_assert(NBUF >= 2 && NBUF <= 4 && TK % 32 == 0, "ring shape");
+  constexpr int LPT = TILEB / (NT * 16);           // DMA instructions per wave per tile
+  static_assert(NBUF >= 2 && NBUF <= 4 && TK % 32 == 0 && LPT >= 1, "ring shape");
   // NBUF key tiles in flight through a ring of LDS buffers filled by direct
   // global->LDS loads.  Separate arrays (indexed statically below) let the
   // compiler see that a DMA into one buffer never aliases reads of another.
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
   const int64_t slab = l * a.Hkv + g;
   const uint8_t* khead = a.kh + slab * a.kh_stride * ROWB;
   const uint8_t* ktail = a.kt + (slab * a.kt_stride + a.kt_row0) * ROWB;
-  const int64_t row_w = rb * kP1Rows + wave * 64;
+  const int64_t row_w = rb * NT + wave * 64;
 
   bf16x8 qf[2][KS];
 #pragma unroll
@@ -112,17 +115,18 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
 
   // Tile layout in LDS: row r (a key), 16-byte chunk c at r*ROWB + ((c ^ (r % CPR)) * 16).
   // The XOR swizzle makes the fragment reads (32 rows, same chunk) hit
-  // distinct banks.  Wave w's i-th DMA fills LDS chunks [(4i+w)*64, +64),
-  // that is RPI whole rows starting at row (4i+w)*RPI, lane by lane, so each
+  // distinct banks.  Wave w's i-th DMA fills LDS chunks [(Wi+w)*64, +64),
+  // that is RPI whole rows starting at row (Wi+w)*RPI, lane by lane, so each
   // lane fetches the global chunk that lands there.  The lane's part of the
   // byte offset (its row within those RPI rows and its swizzled chunk) is the
-  // same for every i and w, because (4i+w)*RPI is a multiple of CPR or adds
-  // the same residue; the instruction's first row rides in the scalar
-  // offset.  That row also picks the buffer (head or tail segment: every
-  // segment boundary is a multiple of RPI), and each buffer resource covers
-  // exactly its segment's rows, so rows past the end read as zero instead of
-  // leaving the slab.
+  // same for every i, because W*RPI is a multiple of CPR (asserted below), so
+  // the rows (Wi+w)*RPI of one wave share their residue mod CPR; the
+  // instruction's first row rides in the scalar offset.  That row also picks
+  // the buffer (head or tail segment: every segment boundary is a multiple of
+  // RPI), and each buffer resource covers exactly its segment's rows, so rows
+  // past the end read as zero instead of leaving the slab.
   constexpr int RPI = 64 / CPR;
+  static_assert((W * RPI) % CPR == 0, "one swizzle residue per wave across its DMAs");
   const __amdgpu_buffer_rsrc_t rs_head = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(khead), (short)0, (int)(uint32_t)(a.split * ROWB), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rs_tail = __builtin_amdgcn_make_buffer_rsrc(
@@ -133,8 +137,8 @@ __global__ __launch_bounds__(kThreads, 2) void pass1_bf16(P1Args a) {
     const int64_t row0 = kbeg + tile * TK;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int64_t rf = row0 + (i * 4 + wave) * RPI;
-      auto* dst = lds_ptr(buf + (i * 4 + wave) * 1024);
+      const int64_t rf = row0 + (i * W + wave) * RPI;
+      auto* dst = lds_ptr(buf + (i * W + wave) * 1024);
       if (rf < a.split)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_head, dst, 16, (int)voff, (int)(uint32_t)(rf * ROWB), 0, 0);
       else
@@ -596,7 +600,9 @@ int run(const kvs_problem& p, const ScorePlan& pl, const void* q, const KvSrc& k
   a1.inv_c1 = inv_c1;
   {
     TraceScope ts("score_pass1_bf16", st);
-    hipLaunchKernelGGL((pass1_bf16<D, kP1Keys, kP1Ring>), dim3((unsigned)pad8(a1.n_logical)), dim3(kThreads), 0, st, a1);
+    static_assert(kP1Waves * 64 == kP1Rows, "planner and kernel agree on the rows per workgroup");
+    hipLaunchKernelGGL((pass1_bf16<D, kP1Keys, kP1Ring, kP1Waves>), dim3((unsigned)pad8(a1.n_logical)),
+                       dim3(kP1Waves * 64), 0, st, a1);
   }
   if (hipError_t e = hipGetLastError()) return (int)e;
   if (pl.splits > 1) {
