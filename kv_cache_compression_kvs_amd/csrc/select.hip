@@ -108,6 +108,14 @@ __device__ __forceinline__ void wave_count(uint32_t* hist, bool active, uint32_t
   if ((act >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
 }
 
+// Word of the LDS key cache that holds candidate i.  Within each 16-word
+// group the low 4 bits are XORed with bits 5-8 of i, so that the ordered
+// sweep's reads (thread t takes kItems = 16 consecutive candidates, 16 words
+// apart from its neighbour's) spread over the banks instead of piling onto a
+// few, while the coalesced reads of consecutive candidates stay conflict-free.
+__device__ __forceinline__ int64_t kswz(int64_t i) { return i ^ ((i >> 5) & 15); }
+static_assert(kItems == 16, "the key cache swizzle is laid out for 16 candidates per thread");
+
 // Radix select and ordered sweep over the nc candidates of one (layer, KV
 // head), keys read from the LDS cache (CACHED) or from global memory.  The
 // choice is made once per workgroup so that no key load sits behind a
@@ -121,10 +129,12 @@ __device__ __forceinline__ void select_body(const float* srow, const uint32_t* k
                                             int64_t nc, int64_t need, int64_t val0) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   auto key_at = [&](int64_t i) __attribute__((always_inline)) -> uint32_t {
-    return CACHED ? keys[i] : order_key(srow[i]);
+    return CACHED ? keys[kswz(i)] : order_key(srow[i]);
   };
 
-  uint32_t tau = 0u;
+  // The candidates kept are those whose key, masked by tmask, is above tau,
+  // and the first e (by position) of those equal to it.
+  uint32_t tau = 0u, tmask = 0xFFFFFFFFu;
   uint32_t e = 0u;
   if (need >= nc) {
     tau = 0u;                 // every candidate is kept
@@ -163,14 +173,21 @@ __device__ __forceinline__ void select_body(const float* srow, const uint32_t* k
       if (tid < 256 && cum >= rem && cum - c < rem) {
         pick[0] = 255u - (uint32_t)tid;
         pick[1] = cum - c;
+        pick[2] = c;  // candidates in the chosen bin
       }
       __syncthreads();
       prefix |= pick[0] << shift;
       mask |= 255u << shift;
       rem -= pick[1];
+      // Every candidate of the chosen bin is kept: the keys above the bin and
+      // the whole bin are exactly the need best, and the lower digits need not
+      // be resolved.  (Equal keys share every bin, so no tie is split.)
+      const bool whole_bin = pick[2] == rem;
       __syncthreads();  // pick is rewritten next round
+      if (whole_bin) break;  // uniform: every thread read the same pick
     }
     tau = prefix;
+    tmask = mask;
     e = rem;
   }
 
@@ -185,8 +202,8 @@ __device__ __forceinline__ void select_body(const float* srow, const uint32_t* k
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
       if (i0 + j < nc) {
-        ngt += x[j] > tau;
-        neq += x[j] == tau;
+        ngt += (x[j] & tmask) > tau;
+        neq += (x[j] & tmask) == tau;
       }
     }
     const uint32_t packed = (ngt << 16) | neq;
@@ -200,11 +217,11 @@ __device__ __forceinline__ void select_body(const float* srow, const uint32_t* k
       const int64_t i = i0 + j;
       // ranks are < need by construction; the bound check only keeps a
       // counting error from ever writing outside this list
-      if (i < nc && x[j] > tau) {
+      if (i < nc && (x[j] & tmask) > tau) {
         const uint64_t rank = gt_before + (eq_before < e ? eq_before : e);
         if (rank < (uint64_t)need) out[rank] = (int32_t)(val0 + i);
         ++gt_before;
-      } else if (i < nc && x[j] == tau) {
+      } else if (i < nc && (x[j] & tmask) == tau) {
         const uint64_t rank = gt_before + eq_before;
         if (eq_before < e && rank < (uint64_t)need) out[rank] = (int32_t)(val0 + i);
         ++eq_before;
@@ -224,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelArgs a) {
   __shared__ uint32_t keys[CACHED ? kLdsKeys : 1];
   __shared__ uint32_t hw[kWaves * 256];
   __shared__ uint32_t wsum[2 * kWaves];
-  __shared__ uint32_t pick[2];
+  __shared__ uint32_t pick[3];
 
   const int tid = threadIdx.x;
   const int64_t unit = blockIdx.x;
@@ -241,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelArgs a) {
   if (need <= 0) return;  // only the sinks (uniform: no barrier skipped by part of the group)
 
   if (CACHED) {
-    for (int64_t i = tid; i < nc; i += kThreads) keys[i] = order_key(srow[i]);
+    for (int64_t i = tid; i < nc; i += kThreads) keys[kswz(i)] = order_key(srow[i]);
     __syncthreads();
   }
   select_body<CACHED>(srow, keys, hw, wsum, pick, out + S, nc, need, S);
@@ -294,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void query_select_kernel(QueryArgs a) {
   __shared__ uint32_t keys[CACHED ? kLdsKeys : 1];
   __shared__ uint32_t hw[kWaves * 256];
   __shared__ uint32_t wsum[2 * kWaves];
-  __shared__ uint32_t pick[2];
+  __shared__ uint32_t pick[3];
   const int64_t r = blockIdx.x;
   const int64_t c0 = a.S + r * a.m;
   const int64_t len = min(a.m, a.N - c0);
@@ -302,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void query_select_kernel(QueryArgs a) {
   const float* srow = a.psum + (c0 - a.S);
   int32_t* out = a.out + r * n_queries_of(a.rho, a.m);
   if (CACHED) {
-    for (int64_t i = threadIdx.x; i < len; i += kThreads) keys[i] = order_key(srow[i]);
+    for (int64_t i = threadIdx.x; i < len; i += kThreads) keys[kswz(i)] = order_key(srow[i]);
     __syncthreads();
   }
   select_body<CACHED>(srow, keys, hw, wsum, pick, out, len, nq, c0);
