@@ -52,7 +52,8 @@ int check(const kvs_problem* p) {
   if (p->dtype == KVS_BF16 && pl.units * pl.splits * pl.row_blocks + 8 > kMaxGrid)
     return KVS_E_SHAPE;
   if (pl.units * pl.n_chunks * std::max<int64_t>(pl.p2_tiles, 1) + 8 > kMaxGrid) return KVS_E_SHAPE;
-  if (pl.total_rows / 256 + 1 > kMaxGrid) return KVS_E_SHAPE;
+  if (pl.total_rows / 256 + 1 > kMaxGrid) return KVS_E_SHAPE;  // the split merge, one row per thread
+  if (p->dtype == KVS_F32 && pl.row_blocks + 1 > kMaxGrid) return KVS_E_SHAPE;
   return KVS_OK;
 }
 
@@ -297,10 +298,10 @@ ScorePlan plan_score(const kvs_problem& p) {
     pl.splits = cdiv(N, pl.keys_per_split);
     pl.p2_tiles = cdiv(chunk_len, kP2Keys);
   } else {
-    pl.row_blocks = cdiv(pl.total_rows, 256);
+    pl.row_blocks = cdiv(pl.total_rows, kF32P1Rows);
     pl.splits = 1;
     pl.keys_per_split = N;
-    pl.p2_tiles = cdiv(chunk_len, 256);
+    pl.p2_tiles = cdiv(chunk_len, kF32P2Keys);
   }
   size_t off = 0;
   pl.off_c2 = off;

@@ -167,5 +167,9 @@ constexpr int kP2Keys = kP2Waves * 64;  // keys per pass-2 workgroup
 constexpr int kP2Ring = 3;        // pass-2 LDS query tiles in flight
 constexpr int kMaxSplits = 64;
 constexpr int kP1Slots = 2048 / kP1Waves;  // resident pass-1 workgroups: 2 waves per SIMD, 1,024 SIMDs
+// fp32 path: query rows per pass-1 workgroup (one wave each) and positions
+// per pass-2 workgroup.
+constexpr int kF32P1Rows = 4;
+constexpr int kF32P2Keys = 64;
 
 }  // namespace kvs
