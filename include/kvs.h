@@ -114,7 +114,11 @@ int64_t kvs_num_chunks(const kvs_problem* p);
 int64_t kvs_num_queries(const kvs_problem* p);
 
 /* Bytes of device workspace kvs_score, kvs_select and kvs_compress_block need
- * for this problem (0 if the problem is invalid).  Host only. */
+ * for this problem (0 if the problem is invalid).  Host only.  On long caches
+ * this includes the per-split statistics that let every pass-1 workgroup
+ * stream at most 32K keys; a call given less workspace, but enough for the
+ * plan without that cap, splits the keys less (scores equal up to rounding),
+ * and a call given too little for that returns KVS_E_WORKSPACE. */
 size_t kvs_workspace_bytes(const kvs_problem* p);
 
 /*
@@ -139,7 +143,8 @@ int kvs_layer_budgets(int32_t layers, int64_t total, const double* sens, double 
  *                     softmax_i'( q[l,h,j] . k[l,g,i'] / sqrt(d) )[i]
  * with the softmax over all N positions; sink positions i < S get 1.0.
  * q, k: device, per the layouts above.  scores: device [L, Hkv, N] fp32, fully
- * written.  ws: device workspace of at least kvs_workspace_bytes(p) bytes.
+ * written.  ws: device workspace, kvs_workspace_bytes(p) bytes for the
+ * planned key split (see there).
  */
 int kvs_score(const kvs_problem* p, const void* q, const void* k, float* scores,
               void* ws, size_t ws_bytes, void* stream);
@@ -203,9 +208,12 @@ int kvs_compress_block(const kvs_problem* p, const void* q, const void* k, const
  * `stream`, or the current device for a NULL stream), which that GPU holds
  * from the first call on it until the process ends.  The call allocates
  * nothing (no hipMalloc, no hipFree, no allocating library routine).
- * Returns KVS_E_SCRATCH, before touching the device, when the problem needs
- * more scratch than that (kvs_workspace_bytes(p) covers it; the 131,072-token
- * KV² shape of 36 layers x 32 query heads needs about 60 MB).  Every call on
+ * Returns KVS_E_SCRATCH, before touching the device, when even the scoring
+ * plan without the key-stream cap (see kvs_workspace_bytes) needs more scratch
+ * than that; the 131,072-token KV² shape of 36 layers x 32 query heads needs
+ * about 60 MB that way.  kvs_compress_block given a larger workspace splits
+ * pass 1's keys further, so the two agree bit for bit when kvs_compress_block
+ * gets a workspace of KVS_NOALLOC_SCRATCH_BYTES. Every call on
  * one GPU shares its array and finds the previous call's contents there; the
  * kernels write everything they read from it first.  Calls that overlap on
  * one GPU (two streams, two threads) race on the array: serialise them.

@@ -2,6 +2,7 @@
 // dispatch to the HIP launchers.  Pure host C++; every check runs before any
 // work is enqueued, so a rejected call leaves all outputs untouched.
 #include <algorithm>
+#include <cassert>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -176,7 +177,7 @@ int check_src(const kvs_problem& p, const KvSrc& kv, bool need_k, bool need_v) {
 
 int do_score(const kvs_problem& p, const void* q, const KvSrc& kv, float* scores, void* ws,
              size_t ws_bytes) {
-  const ScorePlan pl = plan_score(p);
+  const ScorePlan pl = plan_score(p, ws_bytes);
   if (p.n_cache > 0 && !scores) return KVS_E_NULL;
   if (int st = check_src(p, kv, true, false)) return st;
   if (pl.n_queries > 0 && !q) return KVS_E_NULL;
@@ -205,10 +206,11 @@ int check_global(const kvs_problem& p, int64_t total) {
   return KVS_OK;
 }
 
+// ws_bytes must be the size do_score accepted: the plan depends on it.
 int enqueue_score(const kvs_problem& p, const void* q, const KvSrc& kv, float* scores, void* ws,
-                  void* stream) {
+                  size_t ws_bytes, void* stream) {
   if (p.n_cache == 0) return KVS_OK;
-  const ScorePlan pl = plan_score(p);
+  const ScorePlan pl = plan_score(p, ws_bytes);
   if (pl.n_chunks == 0)  // every position is a sink
     return to_status(launch_fill(scores, (int64_t)p.layers * p.kv_heads * p.n_cache, 1.0f, stream));
   if (p.dtype == KVS_BF16) return to_status(launch_score_bf16(p, pl, q, kv, scores, ws, stream));
@@ -244,7 +246,7 @@ int compress(const kvs_problem& p, const void* q, const KvSrc& kv, int64_t total
     return KVS_E_ALIGN;
   if (k_per_layer_out) std::memcpy(k_per_layer_out, kl.data(), sizeof(int64_t) * p.layers);
   if (p.n_cache == 0) return KVS_OK;
-  st = enqueue_score(p, q, kv, scores, ws, stream);
+  st = enqueue_score(p, q, kv, scores, ws, ws_bytes, stream);
   if (st) return st;
   st = to_status(launch_select(p, scores, t, kept, ws, stream));
   if (st) return st;
@@ -254,7 +256,19 @@ int compress(const kvs_problem& p, const void* q, const KvSrc& kv, int64_t total
 
 }  // namespace
 
-ScorePlan plan_score(const kvs_problem& p) {
+namespace {
+
+// Bytes of the scoring workspace: -c2/c1 per row, and (m, l) per row and split
+// when the keys are split.  The layout below carves exactly this.
+size_t score_ws_bytes(int64_t total_rows, int64_t splits) {
+  size_t b = round256(sizeof(float) * (size_t)total_rows);
+  if (splits > 1) b += 2 * round256(sizeof(float) * (size_t)total_rows * (size_t)splits);
+  return b;
+}
+
+}  // namespace
+
+ScorePlan plan_score(const kvs_problem& p, size_t ws_cap) {
   ScorePlan pl;
   const int64_t N = std::max<int64_t>(p.n_cache, 0);
   const int64_t Hkv = std::max(p.kv_heads, 1);
@@ -294,6 +308,13 @@ ScorePlan plan_score(const kvs_problem& p) {
         splits = sp;
       }
     }
+    // Long caches: at most kP1StreamKeys keys per workgroup, if the workspace
+    // holds the statistics of that many splits.
+    const int64_t by_stream = std::min<int64_t>(cdiv(N, kP1StreamKeys), kMaxSplits);
+    if (by_stream > splits) {
+      const int64_t kps = cdiv(cdiv(N, by_stream), kP1Keys) * kP1Keys;
+      if (score_ws_bytes(pl.total_rows, cdiv(N, kps)) <= ws_cap) splits = by_stream;
+    }
     pl.keys_per_split = cdiv(cdiv(N, splits), kP1Keys) * kP1Keys;
     pl.splits = cdiv(N, pl.keys_per_split);
     pl.p2_tiles = cdiv(chunk_len, kP2Keys);
@@ -314,6 +335,7 @@ ScorePlan plan_score(const kvs_problem& p) {
     off += round256(sizeof(float) * (size_t)pl.total_rows * (size_t)pl.splits);
   }
   pl.ws_bytes = off;
+  assert(pl.ws_bytes == score_ws_bytes(pl.total_rows, pl.splits));
   return pl;
 }
 
@@ -367,7 +389,7 @@ int kvs_score(const kvs_problem* p, const void* q, const void* k, float* scores,
   const KvSrc kv = single_src(*p, k, nullptr);
   st = do_score(*p, q, kv, scores, ws, ws_bytes);
   if (st) return st;
-  return enqueue_score(*p, q, kv, scores, ws, stream);
+  return enqueue_score(*p, q, kv, scores, ws, ws_bytes, stream);
 }
 
 int kvs_select(const kvs_problem* p, const float* scores, const int64_t* k_per_layer,
@@ -443,7 +465,7 @@ int kvs_compress_block_noalloc(const kvs_problem* p, const void* q, const void* 
   if (st) return st;
   // scratch the kernels of this call use: the scoring plan's, and the
   // multi-workgroup select's when the cache takes that path
-  size_t need = plan_score(*p).ws_bytes;
+  size_t need = plan_score(*p, KVS_NOALLOC_SCRATCH_BYTES).ws_bytes;
   if (select_uses_multi(*p)) need = std::max(need, select_ws_layout(*p).bytes);
   if (need > (size_t)KVS_NOALLOC_SCRATCH_BYTES) return KVS_E_SCRATCH;
   void* ws = nullptr;
@@ -548,7 +570,7 @@ int kvs_compress_global(const kvs_problem* p, const void* q, const void* k, cons
   if ((kept && !aligned(kept, 4)) || !aligned(offsets, 8) || (k_out && !aligned(k_out, 16)) ||
       (v_out && !aligned(v_out, 16)) || !aligned(ws, 256))
     return KVS_E_ALIGN;
-  if ((st = enqueue_score(*p, q, kv, scores, ws, stream))) return st;
+  if ((st = enqueue_score(*p, q, kv, scores, ws, ws_bytes, stream))) return st;
   if ((st = to_status(launch_select_global(*p, scores, total_budget, kept, offsets, ws, stream))))
     return st;
   if (total_budget == 0) return KVS_OK;

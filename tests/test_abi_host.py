@@ -168,6 +168,25 @@ def test_score_rejects_bad_arguments(K):
     assert h.kvs_score(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, ws, None) == 2
 
 
+def test_long_cache_workspace_sets_the_pass1_split(K):
+    """At the KV² 131K shape kvs_workspace_bytes sizes the plan whose pass-1
+    workgroups stream at most 32K keys (4 splits: -c2/c1 per row plus (m, l)
+    per row and split); a workspace short of even the unsplit plan (-c2/c1 per
+    row only) is refused before anything is enqueued."""
+    h = raw(K)
+    p = prob(K, layers=36, q_heads=32, kv_heads=8, n_cache=131072, chunk_size=4096,
+             q_per_chunk=410)
+    rows = 36 * 32 * 32 * 410
+    r256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    unsplit = r256(4 * rows)
+    assert K.kvs_workspace_bytes(p) == unsplit + 2 * r256(4 * rows * 4)
+    assert h.kvs_score(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, unsplit - 1, None) == 6
+    # a cache of 32K keys is not split for the stream cap
+    p32 = prob(K, layers=32, q_heads=32, kv_heads=8, n_cache=32768, chunk_size=4096,
+               q_per_chunk=410)
+    assert K.kvs_workspace_bytes(p32) < 2 * r256(4 * 32 * 32 * 8 * 410)
+
+
 def test_select_and_compact_reject_bad_budgets(K):
     h = raw(K)
     p = prob(K)
